@@ -1,0 +1,11 @@
+"""Affine group-quantized matmul (qmv / qmm_t) on AMD MI355X (gfx950).
+
+The computation lives in libqmm.so (hand-written HIP kernels behind the C ABI of
+include/qmm.h); this package only marshals torch tensors into those calls.
+"""
+from ._lib import (QMM_BF16, QMM_DECODE_MAX_ROWS, QMM_FLAG_FORCE_STRIDED, QMM_FP16, QmmError,
+                   load)
+from .api import QuantizedWeight, plan, qmm_t, qmv, quantize
+
+__all__ = ["QMM_BF16", "QMM_FP16", "QMM_FLAG_FORCE_STRIDED", "QMM_DECODE_MAX_ROWS", "QmmError",
+           "QuantizedWeight", "load", "plan", "qmm_t", "qmv", "quantize"]

@@ -1,0 +1,112 @@
+"""Python entry points over the C ABI: quantize, qmv, qmm_t, plan.
+
+Argument marshalling only -- every step of the computation runs in libqmm.so's HIP
+kernels.  PyTorch provides device memory and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+_DTYPE_CODE = {torch.bfloat16: _lib.QMM_BF16, torch.float16: _lib.QMM_FP16}
+_DTYPE_NAME = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+@dataclass
+class QuantizedWeight:
+    """Packed codes [N, K*bits/32] (int32 storage of uint32 words), scales/biases [N, K/gs]."""
+    w_packed: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+    N: int
+    K: int
+    group_size: int
+    bits: int
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.scales.dtype
+
+    def desc(self) -> _lib.WeightDesc:
+        d = _lib.WeightDesc()
+        d.w_packed = self.w_packed.data_ptr()
+        d.w_row_stride = self.w_packed.stride(0)
+        d.scales = self.scales.data_ptr()
+        d.biases = self.biases.data_ptr()
+        assert self.scales.stride() == self.biases.stride() and self.scales.stride(1) == 1
+        d.sb_row_stride = self.scales.stride(0)
+        d.N, d.K, d.group_size, d.bits = self.N, self.K, self.group_size, self.bits
+        d.dtype = _DTYPE_CODE[self.scales.dtype]
+        return d
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def quantize(w: torch.Tensor, group_size: int, bits: int, dtype="bf16") -> QuantizedWeight:
+    """Quantize a float32 [N, K] device tensor (qmm_quantize)."""
+    if isinstance(dtype, str):
+        dtype = _DTYPE_NAME[dtype]
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1 and w.is_cuda
+    n, k = w.shape
+    lib = _lib.load()
+    wp = torch.empty(n, k * bits // 32, dtype=torch.int32, device=w.device)
+    sc = torch.empty(n, k // group_size, dtype=dtype, device=w.device)
+    bi = torch.empty_like(sc)
+    _lib.check(lib.qmm_quantize(w.data_ptr(), n, k, w.stride(0), group_size, bits,
+                                _DTYPE_CODE[dtype], wp.data_ptr(), sc.data_ptr(), bi.data_ptr(),
+                                _stream(w.device)))
+    return QuantizedWeight(wp, sc, bi, n, k, group_size, bits)
+
+
+def _matmul(entry, x: torch.Tensor, qw: QuantizedWeight, flags: int = 0,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    lib = _lib.load()
+    y = out if out is not None else torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device)
+    xd = _lib.tensor_desc(x.shape, x.stride())
+    yd = _lib.tensor_desc(y.shape, y.stride())
+    wd = qw.desc()
+    if x.dtype != qw.dtype or y.dtype != qw.dtype:
+        raise _lib.QmmError(-2, "x, y, scales and biases must share one dtype")
+    fn = lib.qmv if entry == 0 else lib.qmm_t
+    _lib.check(fn(x.data_ptr(), ctypes.byref(xd), ctypes.byref(wd), y.data_ptr(), ctypes.byref(yd),
+                  flags, _stream(x.device)))
+    return y
+
+
+def qmv(x: torch.Tensor, qw: QuantizedWeight, flags: int = 0, out=None) -> torch.Tensor:
+    """Decode form, at most 32 collapsed activation rows."""
+    return _matmul(0, x, qw, flags, out)
+
+
+def qmm_t(x: torch.Tensor, qw: QuantizedWeight, flags: int = 0, out=None) -> torch.Tensor:
+    """Transposed matrix-matrix form, any number of rows."""
+    return _matmul(1, x, qw, flags, out)
+
+
+def plan(x_shape, x_stride, N: int, K: int, group_size: int = 64, bits: int = 4,
+         dtype: int = _lib.QMM_BF16, entry: int = 1, flags: int = 0, y_shape=None, y_stride=None) -> dict:
+    """Host-only dispatcher query (qmm_plan): the plan, or QmmError."""
+    lib = _lib.load()
+    if y_shape is None:
+        y_shape = list(x_shape[:-1]) + [N]
+    if y_stride is None:
+        y_stride, acc = [], 1
+        for s in reversed(y_shape):
+            y_stride.insert(0, acc)
+            acc *= s
+    xd = _lib.tensor_desc(x_shape, x_stride)
+    yd = _lib.tensor_desc(y_shape, y_stride)
+    wd = _lib.WeightDesc()
+    wd.w_row_stride = K * bits // 32 + (-(K * bits // 32)) % 4
+    wd.sb_row_stride = K // group_size
+    wd.N, wd.K, wd.group_size, wd.bits, wd.dtype = N, K, group_size, bits, dtype
+    p = _lib.Plan()
+    _lib.check(lib.qmm_plan(ctypes.byref(xd), ctypes.byref(wd), ctypes.byref(yd), flags, entry,
+                            ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in _lib.Plan._fields_}

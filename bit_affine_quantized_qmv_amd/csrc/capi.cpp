@@ -1,0 +1,99 @@
+// extern "C" entry points of libqmm.so: validate, plan, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <string>
+
+#include "../../include/qmm.h"
+#include "dispatch.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+int32_t finish(int32_t rc, const std::string& msg) {
+  g_error = rc == QMM_OK ? std::string() : msg;
+  return rc;
+}
+
+int32_t launch_status(hipError_t e) {
+  if (e == hipSuccess) return finish(QMM_OK, "");
+  return finish(QMM_ERR_HIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+}
+
+int32_t run_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_desc_t* w, void* y,
+                   const qmm_tensor_desc_t* yd, uint32_t flags, void* stream, int entry) {
+  std::string err;
+  qmm_plan_t p;
+  const int rc = qmm::plan_matmul(x, xd, w, y, yd, flags, entry, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0 || w->N == 0) return finish(QMM_OK, "");
+  qmm::MatArgs a;
+  a.x = x;
+  a.batches = p.batches;
+  a.batch_stride = p.batch_stride;
+  a.rows_per_batch = p.rows_per_batch;
+  a.seg_rows = p.seg_rows;
+  a.seg_stride = p.seg_stride;
+  a.row_stride = p.row_stride;
+  a.w = w->w_packed;
+  a.w_row_stride = w->w_row_stride;
+  a.scales = w->scales;
+  a.biases = w->biases;
+  a.sb_row_stride = w->sb_row_stride;
+  a.y = y;
+  a.N = w->N;
+  a.K = w->K;
+  a.group_size = w->group_size;
+  a.bits = w->bits;
+  a.dtype = w->dtype;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_status(p.family == 0 ? qmm::launch_decode(a, s) : qmm::launch_prefill(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qmm_abi_version(void) { return QMM_ABI_VERSION; }
+
+const char* qmm_last_error(void) { return g_error.c_str(); }
+
+int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride, int32_t group_size,
+                     int32_t bits, int32_t dtype, uint32_t* w_packed, void* scales, void* biases,
+                     void* stream) {
+  std::string err;
+  int rc = qmm::check_codec(group_size, bits, dtype, &err);
+  if (rc) return finish(rc, err);
+  if (N < 0 || K <= 0) return finish(QMM_ERR_SHAPE, "need N >= 0 and K > 0");
+  if (K % group_size) return finish(QMM_ERR_SHAPE, "K is not a multiple of group_size");
+  if (w_row_stride < K) return finish(QMM_ERR_SHAPE, "w_row_stride < K");
+  if (N == 0) return finish(QMM_OK, "");
+  if (!w || !w_packed || !scales || !biases)
+    return finish(QMM_ERR_NULL, "w, w_packed, scales and biases must be non-NULL");
+  if ((uintptr_t)w % 4 || (uintptr_t)w_packed % 4 || (uintptr_t)scales % 2 || (uintptr_t)biases % 2)
+    return finish(QMM_ERR_ALIGN, "w/w_packed must be 4-byte and scales/biases 2-byte aligned");
+  qmm::QuantArgs a{w, N, K, w_row_stride, group_size, bits, dtype, w_packed, scales, biases};
+  return launch_status(qmm::launch_quantize(a, (hipStream_t)stream));
+}
+
+int32_t qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+            const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream) {
+  return run_matmul(x, x_desc, w, y, y_desc, flags, stream, 0);
+}
+
+int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+              const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream) {
+  return run_matmul(x, x_desc, w, y, y_desc, flags, stream, 1);
+}
+
+int32_t qmm_plan(const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+                 const qmm_tensor_desc_t* y_desc, uint32_t flags, int32_t entry, qmm_plan_t* out) {
+  std::string err;
+  if (entry != 0 && entry != 1) return finish(QMM_ERR_UNSUPPORTED, "entry must be 0 (qmv) or 1 (qmm_t)");
+  const int rc = qmm::plan_matmul(nullptr, x_desc, w, nullptr, y_desc, flags, entry, false, out, &err);
+  return finish(rc, err);
+}
+
+}  // extern "C"

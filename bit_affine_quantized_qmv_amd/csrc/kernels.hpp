@@ -1,0 +1,53 @@
+// Launch interface between the host dispatcher and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// One matmul call, already validated and planned.  Row r (0 <= r < rows_per_batch) of grid
+// batch z reads x at x + z*batch_stride + (r / seg_rows)*seg_stride + (r % seg_rows)*row_stride
+// and writes y + (z*rows_per_batch + r)*N.
+struct MatArgs {
+  const void* x;
+  int64_t batches;
+  int64_t batch_stride;
+  int64_t rows_per_batch;
+  int64_t seg_rows;
+  int64_t seg_stride;
+  int64_t row_stride;
+  const uint32_t* w;
+  int64_t w_row_stride;
+  const void* scales;
+  const void* biases;
+  int64_t sb_row_stride;
+  void* y;
+  int64_t N;
+  int64_t K;
+  int32_t group_size;
+  int32_t bits;
+  int32_t dtype;  // 1 = bf16, 2 = fp16
+};
+
+struct QuantArgs {
+  const float* w;
+  int64_t N;
+  int64_t K;
+  int64_t w_row_stride;
+  int32_t group_size;
+  int32_t bits;
+  int32_t dtype;
+  uint32_t* w_packed;
+  void* scales;
+  void* biases;
+};
+
+// Decode family: rows_per_batch <= 32.
+hipError_t launch_decode(const MatArgs& a, hipStream_t stream);
+// MFMA prefill: any rows_per_batch.
+hipError_t launch_prefill(const MatArgs& a, hipStream_t stream);
+// Min/max group quantizer.
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+}  // namespace qmm

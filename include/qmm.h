@@ -1,0 +1,157 @@
+/*
+ * qmm.h -- C ABI of the affine group-quantized matmul library (libqmm.so, gfx950).
+ *
+ * Operation:  y = x . dequant(W)^T with w[n,k] = s[n,g] * q[n,k] + b[n,g], g = k / group_size.
+ * (huggingface/transformers issue 47331, section "Root cause": the kernel call
+ *  affine_qmm_t(x, w_packed, scales, biases, group_size, bits) returns y of shape
+ *  x.shape[:-1] + [N]; "Fix": a batched input must give the same rows as the same input
+ *  flattened to 2D.)
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers.  Descriptors are HOST pointers, read during the
+ *     call only.  The caller owns all memory; the library allocates nothing and keeps no
+ *     state besides a thread-local error message.
+ *   - Strides are in elements.  A tensor pointer points at the view's first element (a view's
+ *     storage offset is already applied).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued asynchronously;
+ *     the library never synchronizes.
+ *   - Every argument is validated before anything is launched; on error nothing is written,
+ *     the call returns a negative QMM_ERR_* code and qmm_last_error() describes it
+ *     (candle pitfall page "Metal 上批量 matmul 结果不对", section 现象: a structured error that
+ *     names the layout is preferred over a silently wrong result).
+ *   - dtype of x, scales, biases and y is one and the same: QMM_BF16 or QMM_FP16.
+ *   - bits in {2,3,4,5,6,8}; group_size in {32,64,128}; K % group_size == 0.
+ *   - Codes are a little-endian bitstream per weight row: code k of row n sits at bit k*bits
+ *     of the row's stream of uint32 words, continuing into the next word when it straddles
+ *     one (Metal Kernel Bits=8 final report, section 3.1, gives the 4- and 8-bit cases).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMM_ABI_VERSION 1
+#define QMM_MAX_DIMS 8
+/* Collapsed activation rows up to this count use the decode (qmv) kernels. */
+#define QMM_DECODE_MAX_ROWS 32
+
+typedef enum { QMM_BF16 = 1, QMM_FP16 = 2 } qmm_dtype_t;
+
+/* Return codes. */
+enum {
+  QMM_OK = 0,
+  QMM_ERR_NULL = -1,        /* a required pointer is NULL                                  */
+  QMM_ERR_UNSUPPORTED = -2, /* bits / group_size / dtype / flag not supported              */
+  QMM_ERR_SHAPE = -3,       /* shapes disagree (K, N, y shape, K % group_size, qmv rows)    */
+  QMM_ERR_LAYOUT = -4,      /* x batch dims cannot be expressed as <= 2 strided levels, a   */
+                            /* negative stride, x last-dim stride != 1, or y not dense      */
+  QMM_ERR_ALIGN = -5,       /* pointer / stride / K alignment that the kernels require      */
+  QMM_ERR_HIP = -6          /* the HIP runtime reported an error at launch                  */
+};
+
+/* Flags for qmv / qmm_t. */
+enum {
+  /* Do not fold the batch dims: launch one grid slice per batch element, each of which
+   * re-reads the whole weight.  Results are bitwise identical to the folded launch; it
+   * exists to time the per-batch-element path against the folded one
+   * (transformers issue 47331 summary page, 原因分析: 60 ms vs 2.2 ms for [32,1,K]). */
+  QMM_FLAG_FORCE_STRIDED = 1u << 0
+};
+
+typedef struct {
+  int32_t ndim;                   /* 1 .. QMM_MAX_DIMS                                    */
+  int64_t shape[QMM_MAX_DIMS];
+  int64_t stride[QMM_MAX_DIMS];   /* elements, >= 0                                        */
+} qmm_tensor_desc_t;
+
+typedef struct {
+  const uint32_t* w_packed; /* device, row n at w_packed + n * w_row_stride                 */
+  int64_t w_row_stride;     /* uint32 words, >= K*bits/32; the matmul needs a multiple of 4 */
+  const void* scales;       /* device, [N, sb_row_stride] of dtype                          */
+  const void* biases;       /* device, [N, sb_row_stride] of dtype                          */
+  int64_t sb_row_stride;    /* elements, >= K / group_size                                  */
+  int64_t N;                /* output features (weight rows)                                */
+  int64_t K;                /* input features                                               */
+  int32_t group_size;
+  int32_t bits;
+  int32_t dtype;            /* qmm_dtype_t                                                  */
+} qmm_weight_desc_t;
+
+/* How a call is executed; filled by qmm_plan (host only, no GPU needed).
+ * Row r (0 <= r < rows_per_batch) of grid batch z reads x at
+ *   x + z*batch_stride + (r / seg_rows)*seg_stride + (r % seg_rows)*row_stride
+ * and writes y at y + (z*rows_per_batch + r)*N. */
+typedef struct {
+  int64_t rows;            /* total collapsed activation rows M                          */
+  int64_t batches;         /* grid batch slices (1 unless QMM_FLAG_FORCE_STRIDED)         */
+  int64_t batch_stride;
+  int64_t rows_per_batch;
+  int64_t seg_rows;        /* rows per contiguous-stride segment                          */
+  int64_t seg_stride;
+  int64_t row_stride;
+  int32_t family;          /* 0: decode kernels (rows <= QMM_DECODE_MAX_ROWS), 1: prefill */
+  int32_t kind;            /* 0: folded to one 2D matrix, 1: two strided levels,          */
+                           /* 2: one grid slice per batch element (forced)                */
+} qmm_plan_t;
+
+/* Version of this ABI (QMM_ABI_VERSION). */
+int32_t qmm_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until the next call
+ * into the library on the same thread. */
+const char* qmm_last_error(void);
+
+/* Quantize W [N, K] (float32, row n at w + n*w_row_stride) per row and per group of
+ * group_size columns with min/max affine parameters (transformers issue 47331, "Root
+ * cause": quantize, then cast scales and biases to the storage dtype):
+ *   s = fl32(fl32(max - min) / (2^bits - 1)),  b = min,
+ *   q = clamp(round_half_even(fl32(fl32(w - b) / s)), 0, 2^bits - 1)   (q = 0 when s == 0),
+ * scales/biases stored as s, b rounded to nearest-even in dtype.
+ * Outputs are dense: w_packed [N, K*bits/32] words, scales and biases [N, K/group_size].
+ * Requires K % group_size == 0 and finite inputs.  N == 0 is a no-op. */
+int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride,
+                     int32_t group_size, int32_t bits, int32_t dtype,
+                     uint32_t* w_packed, void* scales, void* biases, void* stream);
+
+/* Matrix-vector form for decode: y = x . dequant(W)^T where the collapsed activation rows
+ * number at most QMM_DECODE_MAX_ROWS (otherwise QMM_ERR_SHAPE: use qmm_t).
+ * x: shape [..., K] (any rank 1..8), last-dim stride 1, other strides >= 0.  Batch dims
+ *    are folded when their strides allow (candle pitfall page, 怎么确认没中招: dims i, i+1
+ *    merge iff stride[i] == stride[i+1]*shape[i+1]; size-1 dims always merge); at most two
+ *    strided levels may remain, otherwise QMM_ERR_LAYOUT.
+ * y: dense row-major, shape x.shape[:-1] + [N].
+ * Every row's arithmetic is independent of how many rows share the call, so row i of a
+ * batched call is bit-identical to a call on row i alone (MLX pull request 4516,
+ * "Correctness": bitwise-identical outputs over decode steps).
+ * Sums of x are taken in float32 after widening each element (MLX pull request 4516,
+ * first commit: widen each input before adding it to the bias * sum(x) term).
+ * Alignment: x, w_packed 16-byte aligned; x strides (except the last) multiples of 8;
+ * w_row_stride a multiple of 4; K a multiple of 128.
+ * M == 0 or N == 0 is a no-op returning QMM_OK. */
+int32_t qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+            void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
+
+/* Transposed matrix-matrix form (prefill and batched decode): same operation and contract
+ * as qmv, any number of rows.  Up to QMM_DECODE_MAX_ROWS collapsed rows it runs the same
+ * kernels as qmv (so the results agree bitwise); beyond that it runs the MFMA prefill
+ * kernel, which dequantizes weight tiles to dtype in LDS before the products. */
+int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+              void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
+
+/* Host-only: validate a qmv (entry = 0) or qmm_t (entry = 1) call and report its plan
+ * without touching the GPU.  Pointers inside `w` are only checked for NULL/alignment when
+ * they are non-NULL (pass NULLs to test layouts alone).  Returns QMM_OK or the same error
+ * code the call itself would return. */
+int32_t qmm_plan(const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+                 const qmm_tensor_desc_t* y_desc, uint32_t flags, int32_t entry,
+                 qmm_plan_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */
