@@ -1,0 +1,288 @@
+// Decode-family kernels and their launchers (instantiated per code width in decode_b*.hip).
+//
+// qmv_stream_kernel: the activations (all rows, all K) stay resident in LDS; every wave
+//   owns a contiguous range of 16-row weight tiles and streams them through a ring of
+//   DEPTH slots of in-flight 16-byte loads, so the HBM stream never waits on the MFMAs.
+//   The first loads are issued before the activations are staged.
+// qmv_chunk_kernel: for activations too large for LDS; K is processed in chunks staged
+//   one after another, each wave keeping TN tiles' accumulators across chunks.
+// Both compute exactly the per-element arithmetic described in decode_impl.hpp.
+#pragma once
+
+#include "decode_impl.hpp"
+
+namespace qmm {
+namespace decode {
+
+constexpr int kStreamDepth = 6;
+constexpr int kChunkTiles = 2;
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int kChunkXBytes = 64 * 1024;
+
+template <class T, int BITS, int GS, int MT, int DEPTH>
+__global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, const int tiles_base,
+                                                              const int tiles_rem) {
+  using S = Slot<BITS, GS>;
+  constexpr int MROWS = 16 * MT;
+  extern __shared__ u32x4 smem[];
+  const int K = (int)a.K;
+  u32x4* xs = smem;
+  float* sxs = (float*)(smem + (K / 32) * 4 * MROWS);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  constexpr bool kBuf = BITS == 4 || BITS == 8;
+  // The buffer-descriptor path needs the wave index in a scalar register.  The other code
+  // widths keep it per lane: their fp16 instantiations gave run-to-run different results
+  // with the scalar form, and that form buys them nothing.
+  const int wave = kBuf ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
+  const int lg = lane >> 4;
+  const int col = lane & 15;
+  const int64_t z = blockIdx.z;
+  const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
+  const int rows = (int)a.rows_per_batch;
+  const int64_t N = a.N;
+  uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
+  const int w_row_bytes = (int)(a.w_row_stride * 4);
+  const int sb_row_bytes = (int)(a.sb_row_stride * 2);
+  const int w_voff = col * w_row_bytes + 16 * lg;
+  const int sb_voff = col * sb_row_bytes;
+
+  // balanced split of the 16-row tiles over the grid's waves: the first tiles_rem waves take
+  // tiles_base + 1 tiles, the others tiles_base (both computed on the host)
+  const int wid = (int)blockIdx.x * kWaves + wave;
+  const int64_t t_begin = (int64_t)wid * tiles_base + min(wid, tiles_rem);
+  const int64_t t_end = t_begin + tiles_base + (wid < tiles_rem ? 1 : 0);
+  const int nit = K / S::kSpan;
+  const int64_t total = (t_end - t_begin) * nit;
+  const int row_words = (K * BITS) >> 5;
+
+  int gword = 0;
+  uint32_t gshift = 0;
+  if constexpr (BITS != 4 && BITS != 8) generic_lane_offsets<BITS>(lg, gword, gshift);
+
+  SlotData<BITS, GS> ring[DEPTH];
+  int64_t ld_tile = t_begin;
+  int ld_kit = 0;
+  auto issue = [&](SlotData<BITS, GS>& d) {
+    // past the wave's last slot: reload that last slot (cache hit, never consumed)
+    const bool live = ld_tile < t_end;
+    const int64_t tile = live ? ld_tile : t_end - 1;
+    const int kit = live ? ld_kit : nit - 1;
+    if constexpr (kBuf) {
+      // one descriptor per 16-row tile, built in scalar registers; rows past N are outside
+      // its range and read as zero (their results are never stored)
+      const int64_t r0 = tile * 16;
+      const int valid = (int)(N - r0 < 16 ? N - r0 : 16);
+      const auto w_rs = make_rsrc(a.w + r0 * a.w_row_stride, (uint32_t)(valid * w_row_bytes));
+      const auto s_rs = make_rsrc((const uint16_t*)a.scales + r0 * a.sb_row_stride, (uint32_t)(valid * sb_row_bytes));
+      const auto b_rs = make_rsrc((const uint16_t*)a.biases + r0 * a.sb_row_stride, (uint32_t)(valid * sb_row_bytes));
+      load_slot_buf<BITS, GS>(d, w_rs, s_rs, b_rs, w_voff, kit * S::kRowWordsPerSlot * 4, sb_voff,
+                              kit * S::kGroups * 2);
+    } else {
+      const int64_t n = tile * 16 + col;
+      const int64_t nl = n < N ? n : N - 1;
+      const uint32_t* wrow = a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot;
+      const uint16_t* srow = (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups;
+      const uint16_t* brow = (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups;
+      load_slot<BITS, GS>(d, wrow, srow, brow, lg, gword, row_words - kit * S::kRowWordsPerSlot);
+    }
+    if (live && ++ld_kit == nit) {
+      ld_kit = 0;
+      ++ld_tile;
+    }
+  };
+
+  if (total > 0) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) issue(ring[j]);
+  }
+  stage_x<T, BITS, MROWS>(xs, a, xb, rows, 0, K, tid, kThreads);
+  __syncthreads();
+  sum_x<T, GS, MT>(xs, sxs, K, wave, kWaves, lane);
+  __syncthreads();
+  if (total == 0) return;
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MT], part[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt] = zero4;
+    part[mt] = zero4;
+  }
+  int64_t cs_tile = t_begin;
+  int cs_kit = 0;
+  auto finish_slot = [&]() {
+    if (++cs_kit == nit) {
+      store_tile<T, MT>(acc, yb, rows, cs_tile * 16 + col, N, lg);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4;
+      cs_kit = 0;
+      ++cs_tile;
+    }
+  };
+
+  const int64_t full = total - total % DEPTH;
+  for (int64_t it = 0; it < full; it += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, cs_kit * S::kSpan, acc, part, lg, col, gshift);
+      issue(ring[j]);
+      finish_slot();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) {
+    if (full + j < total) {
+      consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, cs_kit * S::kSpan, acc, part, lg, col, gshift);
+      finish_slot();
+    }
+  }
+}
+
+template <class T, int BITS, int GS, int MT, int TN>
+__global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
+  using S = Slot<BITS, GS>;
+  constexpr int MROWS = 16 * MT;
+  constexpr int KC = kChunkXBytes / (MROWS * 2);
+  __shared__ u32x4 xs[kChunkXBytes / 16];
+  __shared__ float sxs[(KC / 32) * MROWS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lg = lane >> 4;
+  const int col = lane & 15;
+  const int64_t z = blockIdx.z;
+  const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
+  const int rows = (int)a.rows_per_batch;
+  const int64_t N = a.N;
+  const int K = (int)a.K;
+  const int row_words = (K * BITS) >> 5;
+  uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
+
+  int gword = 0;
+  uint32_t gshift = 0;
+  if constexpr (BITS != 4 && BITS != 8) generic_lane_offsets<BITS>(lg, gword, gshift);
+
+  int64_t nrow[TN], nl[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    nrow[t] = ((int64_t)(blockIdx.x * kWaves + wave) * TN + t) * 16 + col;
+    nl[t] = nrow[t] < N ? nrow[t] : N - 1;
+  }
+  auto issue = [&](SlotData<BITS, GS> (&d)[TN], int kit) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+      load_slot<BITS, GS>(d[t], a.w + nl[t] * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
+                          (const uint16_t*)a.scales + nl[t] * a.sb_row_stride + kit * S::kGroups,
+                          (const uint16_t*)a.biases + nl[t] * a.sb_row_stride + kit * S::kGroups, lg, gword,
+                          row_words - kit * S::kRowWordsPerSlot);
+  };
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[TN][MT], part[TN][MT];
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[t][mt] = zero4;
+      part[t][mt] = zero4;
+    }
+
+  const int nit_total = K / S::kSpan;
+  SlotData<BITS, GS> cur[TN], nxt[TN];
+  issue(cur, 0);
+  for (int kc0 = 0; kc0 < K; kc0 += KC) {
+    const int kcl = min(KC, K - kc0);
+    __syncthreads();
+    stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads);
+    __syncthreads();
+    sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane);
+    __syncthreads();
+    const int kit0 = kc0 / S::kSpan;
+    const int nit = kcl / S::kSpan;
+    for (int i = 0; i < nit; ++i) {
+      const int kit = kit0 + i;
+      issue(nxt, min(kit + 1, nit_total - 1));
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        consume_slot<T, BITS, GS, MT>(cur[t], xs, sxs, i * S::kSpan, acc[t], part[t], lg, col, gshift);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) cur[t] = nxt[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TN; ++t) store_tile<T, MT>(acc[t], yb, rows, nrow[t], N, lg);
+}
+
+// ----------------------------------------------------------------------------- launchers
+int device_cus();
+
+template <class T, int BITS, int GS, int MT>
+hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
+  auto kern = qmv_stream_kernel<T, BITS, GS, MT, kStreamDepth>;
+  static int per_cu = -1;  // occupancy for this instantiation (same LDS class each call)
+  static int lds_cached = -1;
+  if (lds_cached != lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, lds);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+    lds_cached = lds;
+  }
+  const int64_t n_tiles = (a.N + 15) / 16;
+  const int64_t max_waves = (int64_t)device_cus() * per_cu * kWaves;
+  const int64_t per_wave = (n_tiles + max_waves - 1) / max_waves;      // tiles per wave
+  const int64_t waves = (n_tiles + per_wave - 1) / per_wave;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  const int64_t waves_total = blocks * kWaves;
+  if (n_tiles / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kThreads), lds, stream, a,
+                     (int)(n_tiles / waves_total), (int)(n_tiles % waves_total));
+  return hipGetLastError();
+}
+
+template <class T, int BITS, int GS, int MT>
+hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
+  const int64_t rows_per_wg = (int64_t)kWaves * kChunkTiles * 16;
+  dim3 grid((unsigned)((a.N + rows_per_wg - 1) / rows_per_wg), 1, (unsigned)a.batches);
+  hipLaunchKernelGGL((qmv_chunk_kernel<T, BITS, GS, MT, kChunkTiles>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int MT, int GS>
+constexpr int stream_lds_bytes(int K) {
+  return 16 * MT * K * 2 + (K / GS) * 16 * MT * 4;
+}
+
+template <class T, int BITS, int GS>
+hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
+  const int K = (int)a.K;
+  if (a.rows_per_batch <= 16) {
+    const int lds = stream_lds_bytes<1, GS>(K);
+    return lds <= kLdsLimit ? launch_stream<T, BITS, GS, 1>(a, stream, lds) : launch_chunk<T, BITS, GS, 1>(a, stream);
+  }
+  const int lds = stream_lds_bytes<2, GS>(K);
+  return lds <= kLdsLimit ? launch_stream<T, BITS, GS, 2>(a, stream, lds) : launch_chunk<T, BITS, GS, 2>(a, stream);
+}
+
+template <int BITS>
+hipError_t launch_bits(const MatArgs& a, hipStream_t stream) {
+  const bool bf = a.dtype == 1;
+  switch (a.group_size) {
+    case 32: return bf ? launch_gs<Bf16, BITS, 32>(a, stream) : launch_gs<Fp16, BITS, 32>(a, stream);
+    case 64: return bf ? launch_gs<Bf16, BITS, 64>(a, stream) : launch_gs<Fp16, BITS, 64>(a, stream);
+    case 128: return bf ? launch_gs<Bf16, BITS, 128>(a, stream) : launch_gs<Fp16, BITS, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_b4(const MatArgs& a, hipStream_t stream);
+hipError_t launch_decode_b8(const MatArgs& a, hipStream_t stream);
+hipError_t launch_decode_bn(const MatArgs& a, hipStream_t stream);
+
+}  // namespace decode
+}  // namespace qmm

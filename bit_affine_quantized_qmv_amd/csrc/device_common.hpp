@@ -33,6 +33,11 @@ struct Bf16 {
     v2 v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // Two small non-negative integers (< 256, exact in 8 significand bits) as a bf16 pair:
+  // the upper halves of their float32 patterns, joined with one byte permute.
+  __device__ static inline uint32_t pack2_int(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
   // Two fp8 (e4m3) bytes of `w` -> two values, times 2^9.  e4m3 byte patterns 0..15 encode
   // exactly c * 2^-9 (subnormals and the first normal binade share that spacing), so a
   // 4-bit code placed in a byte comes back as the exact integer code.
@@ -60,6 +65,11 @@ struct Fp16 {
   __device__ static inline uint32_t pack2(float lo, float hi) {
     v2 v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  // Two small non-negative integers (< 2048, exact in binary16) as an fp16 pair; the
+  // truncating pack is exact here.
+  __device__ static inline uint32_t pack2_int(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
   __device__ static inline uint32_t fp8x2_lo(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, false));
@@ -92,10 +102,10 @@ __device__ inline u32x4 codes4_to_v8(uint32_t w) {
 template <class T>
 __device__ inline u32x4 codes8_to_v8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r.x = T::pack2((float)(w0 & 0xFFu), (float)((w0 >> 8) & 0xFFu));
-  r.y = T::pack2((float)((w0 >> 16) & 0xFFu), (float)(w0 >> 24));
-  r.z = T::pack2((float)(w1 & 0xFFu), (float)((w1 >> 8) & 0xFFu));
-  r.w = T::pack2((float)((w1 >> 16) & 0xFFu), (float)(w1 >> 24));
+  r.x = T::pack2_int((float)(w0 & 0xFFu), (float)((w0 >> 8) & 0xFFu));
+  r.y = T::pack2_int((float)((w0 >> 16) & 0xFFu), (float)(w0 >> 24));
+  r.z = T::pack2_int((float)(w1 & 0xFFu), (float)((w1 >> 8) & 0xFFu));
+  r.w = T::pack2_int((float)((w1 >> 16) & 0xFFu), (float)(w1 >> 24));
   return r;
 }
 
@@ -109,10 +119,10 @@ __device__ inline u32x4 codesN_to_v8(uint32_t lo, uint32_t hi, uint32_t shift) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = (float)((uint32_t)(v >> (i * BITS)) & mask);
   u32x4 r;
-  r.x = T::pack2(f[0], f[1]);
-  r.y = T::pack2(f[2], f[3]);
-  r.z = T::pack2(f[4], f[5]);
-  r.w = T::pack2(f[6], f[7]);
+  r.x = T::pack2_int(f[0], f[1]);
+  r.y = T::pack2_int(f[2], f[3]);
+  r.z = T::pack2_int(f[4], f[5]);
+  r.w = T::pack2_int(f[6], f[7]);
   return r;
 }
 
