@@ -207,24 +207,79 @@ __device__ inline void generic_lane_offsets(int lg, int& word, uint32_t& shift) 
   shift = (uint32_t)(bit0 & 31);
 }
 
-// Stage activation rows [0, MROWS) x k in [k_begin, k_begin + k_len) into LDS in MFMA
+// Staging of activation rows [0, MROWS) x k in [k_begin, k_begin + k_len) into LDS in MFMA
 // operand order: entry ((step * 4 + lane_group) * MROWS + m) holds 8 values.
+//
+// Thread t always handles activation row m = t % MROWS (the thread count is a multiple of
+// MROWS) and 8-k chunks j8 = t / MROWS, t / MROWS + nthreads / MROWS, ...  Loads are issued
+// in batches of kStageBatch with clamped (always valid) addresses and no branches, so a
+// caller can issue a batch, then other loads, and only then wait for the batch: the memory
+// counter retires loads in issue order, and a load issued after the weight prefetch would
+// make the activation staging wait for the whole prefetch.
+constexpr int kStageBatch = 8;
+
+template <int MROWS>
+struct XStage {
+  u32x4 v[kStageBatch];
+};
+
+template <class T, int BITS, int MROWS>
+__device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb, int rows, int tid) {
+  const int m = tid % MROWS;
+  const int mr = m < rows ? m : 0;   // rows past the call's rows read row 0, stored as zero
+  return xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride;
+}
+
+template <class T, int BITS, int MROWS>
+__device__ inline void stage_x_issue(XStage<MROWS>& st, const uint16_t* xr, int k_begin, int k_len, int batch,
+                                     int tid, int nthreads) {
+  const int c8 = k_len >> 3;
+  const int per = nthreads / MROWS;       // chunks advanced per pass
+  const int j0 = tid / MROWS + batch * kStageBatch * per;
+#pragma unroll
+  for (int b = 0; b < kStageBatch; ++b) {
+    int j8 = j0 + b * per;
+    j8 = j8 < c8 ? j8 : 0;
+    st.v[b] = *(const u32x4*)(xr + k_begin + 8 * j8);
+  }
+}
+
+template <class T, int BITS, int MROWS>
+__device__ inline void stage_x_commit(const XStage<MROWS>& st, u32x4* xs, int rows, int k_len, int batch, int tid,
+                                      int nthreads) {
+  const int c8 = k_len >> 3;
+  const int per = nthreads / MROWS;
+  const int m = tid % MROWS;
+  const int j0 = tid / MROWS + batch * kStageBatch * per;
+#pragma unroll
+  for (int b = 0; b < kStageBatch; ++b) {
+    const int j8 = j0 + b * per;
+    if (j8 < c8) {
+      u32x4 u = m < rows ? st.v[b] : u32x4{0u, 0u, 0u, 0u};
+      if (BITS == 4) u = interleave_even_odd(u);
+      xs[((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) * MROWS + m] = u;
+    }
+  }
+}
+
+// Number of staging batches for a chunk of k_len.
+template <int MROWS>
+__device__ inline int stage_batches(int k_len, int nthreads) {
+  const int per = nthreads / MROWS;
+  const int c8 = k_len >> 3;
+  return (c8 + kStageBatch * per - 1) / (kStageBatch * per);
+}
+
+// Whole staging in one call (used where nothing is in flight that must not be waited for).
 template <class T, int BITS, int MROWS>
 __device__ inline void stage_x(u32x4* xs, const MatArgs& a, const uint16_t* xb, int rows, int k_begin,
                                int k_len, int tid, int nthreads) {
-  // consecutive threads take consecutive rows of one 8-k chunk, so their LDS writes are
-  // consecutive 16-byte entries (no bank conflicts)
-  const int c8 = k_len >> 3;
-  for (int i = tid; i < MROWS * c8; i += nthreads) {
-    const int j8 = i / MROWS;
-    const int m = i - j8 * MROWS;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (m < rows) {
-      const uint16_t* xr = xb + (m / a.seg_rows) * a.seg_stride + (m % a.seg_rows) * a.row_stride;
-      v = *(const u32x4*)(xr + k_begin + 8 * j8);
-    }
-    if (BITS == 4) v = interleave_even_odd(v);
-    xs[((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) * MROWS + m] = v;
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
+  const int nb = stage_batches<MROWS>(k_len, nthreads);
+  for (int batch = 0; batch < nb; ++batch) {
+    XStage<MROWS> st;
+    stage_x_issue<T, BITS, MROWS>(st, xr, k_begin, k_len, batch, tid, nthreads);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, k_len, batch, tid, nthreads);
   }
 }
 

@@ -9,6 +9,8 @@
 // Both compute exactly the per-element arithmetic described in decode_impl.hpp.
 #pragma once
 
+#include <algorithm>
+
 #include "decode_impl.hpp"
 
 namespace qmm {
@@ -62,45 +64,69 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
   if constexpr (BITS != 4 && BITS != 8) generic_lane_offsets<BITS>(lg, gword, gshift);
 
   SlotData<BITS, GS> ring[DEPTH];
+  // Load-stream position: (ld_tile, ld_kit).  After the wave's last slot the stream stays
+  // on that slot (its reloads hit in cache and are never consumed).
   int64_t ld_tile = t_begin;
   int ld_kit = 0;
+  // buffer path: per-tile descriptors (rebuilt only when the stream enters a new tile) and
+  // byte offsets of the slot inside the row (advanced by constants)
+  const int64_t w_tile_words = 16 * a.w_row_stride;
+  const int64_t sb_tile_elems = 16 * a.sb_row_stride;
+  __amdgpu_buffer_rsrc_t w_rs, s_rs, b_rs;
+  int w_soff = 0, sb_soff = 0;
+  auto make_tile_rsrc = [&](int64_t tile) {
+    const int64_t r0 = tile * 16;
+    const int valid = (int)(N - r0 < 16 ? N - r0 : 16);
+    w_rs = make_rsrc(a.w + tile * w_tile_words, (uint32_t)(valid * w_row_bytes));
+    s_rs = make_rsrc((const uint16_t*)a.scales + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
+    b_rs = make_rsrc((const uint16_t*)a.biases + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
+  };
+  if constexpr (kBuf) make_tile_rsrc(t_begin < t_end ? t_begin : 0);
   auto issue = [&](SlotData<BITS, GS>& d) {
-    // past the wave's last slot: reload that last slot (cache hit, never consumed)
-    const bool live = ld_tile < t_end;
-    const int64_t tile = live ? ld_tile : t_end - 1;
-    const int kit = live ? ld_kit : nit - 1;
     if constexpr (kBuf) {
-      // one descriptor per 16-row tile, built in scalar registers; rows past N are outside
-      // its range and read as zero (their results are never stored)
-      const int64_t r0 = tile * 16;
-      const int valid = (int)(N - r0 < 16 ? N - r0 : 16);
-      const auto w_rs = make_rsrc(a.w + r0 * a.w_row_stride, (uint32_t)(valid * w_row_bytes));
-      const auto s_rs = make_rsrc((const uint16_t*)a.scales + r0 * a.sb_row_stride, (uint32_t)(valid * sb_row_bytes));
-      const auto b_rs = make_rsrc((const uint16_t*)a.biases + r0 * a.sb_row_stride, (uint32_t)(valid * sb_row_bytes));
-      load_slot_buf<BITS, GS>(d, w_rs, s_rs, b_rs, w_voff, kit * S::kRowWordsPerSlot * 4, sb_voff,
-                              kit * S::kGroups * 2);
+      load_slot_buf<BITS, GS>(d, w_rs, s_rs, b_rs, w_voff, w_soff, sb_voff, sb_soff);
     } else {
-      const int64_t n = tile * 16 + col;
+      const int64_t n = ld_tile * 16 + col;
       const int64_t nl = n < N ? n : N - 1;
-      const uint32_t* wrow = a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot;
-      const uint16_t* srow = (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups;
-      const uint16_t* brow = (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups;
-      load_slot<BITS, GS>(d, wrow, srow, brow, lg, gword, row_words - kit * S::kRowWordsPerSlot);
+      const uint32_t* wrow = a.w + nl * a.w_row_stride + (int64_t)ld_kit * S::kRowWordsPerSlot;
+      const uint16_t* srow = (const uint16_t*)a.scales + nl * a.sb_row_stride + ld_kit * S::kGroups;
+      const uint16_t* brow = (const uint16_t*)a.biases + nl * a.sb_row_stride + ld_kit * S::kGroups;
+      load_slot<BITS, GS>(d, wrow, srow, brow, lg, gword, row_words - ld_kit * S::kRowWordsPerSlot);
     }
-    if (live && ++ld_kit == nit) {
-      ld_kit = 0;
+    if (ld_kit + 1 < nit) {
+      ++ld_kit;
+      w_soff += S::kRowWordsPerSlot * 4;
+      sb_soff += S::kGroups * 2;
+    } else if (ld_tile + 1 < t_end) {
       ++ld_tile;
+      ld_kit = 0;
+      w_soff = 0;
+      sb_soff = 0;
+      if constexpr (kBuf) make_tile_rsrc(ld_tile);
     }
   };
 
-  if (total > 0) {
+  // activations first (their loads must retire before the weight prefetch), then the
+  // prefetch, then the LDS writes of the first staging batch, then any further batches
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
+  const int nbatch = stage_batches<MROWS>(K, kThreads);
+  {
+    XStage<MROWS> st;
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kThreads);
+    // unconditional (no branch may separate these loads from the staging batch's wait); a
+    // wave without tiles loads valid rows it never consumes
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) issue(ring[j]);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kThreads);
   }
-  stage_x<T, BITS, MROWS>(xs, a, xb, rows, 0, K, tid, kThreads);
-  __syncthreads();
+  for (int batch = 1; batch < nbatch; ++batch) {
+    XStage<MROWS> st;
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kThreads);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kThreads);
+  }
+  lds_barrier();
   sum_x<T, GS, MT>(xs, sxs, K, wave, kWaves, lane);
-  __syncthreads();
+  lds_barrier();
   if (total == 0) return;
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -195,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   issue(cur, 0);
   for (int kc0 = 0; kc0 < K; kc0 += KC) {
     const int kcl = min(KC, K - kc0);
-    __syncthreads();
+    lds_barrier();
     stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads);
-    __syncthreads();
+    lds_barrier();
     sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane);
-    __syncthreads();
+    lds_barrier();
     const int kit0 = kc0 / S::kSpan;
     const int nit = kcl / S::kSpan;
     for (int i = 0; i < nit; ++i) {
@@ -233,11 +259,10 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
     per_cu = nb > 0 ? nb : 1;
     lds_cached = lds;
   }
+  // one full wave of workgroups (every CU at its occupancy), tiles spread over all waves
   const int64_t n_tiles = (a.N + 15) / 16;
-  const int64_t max_waves = (int64_t)device_cus() * per_cu * kWaves;
-  const int64_t per_wave = (n_tiles + max_waves - 1) / max_waves;      // tiles per wave
-  const int64_t waves = (n_tiles + per_wave - 1) / per_wave;
-  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  const int64_t full = (int64_t)device_cus() * per_cu;
+  const int64_t blocks = std::min<int64_t>(full, (n_tiles + kWaves - 1) / kWaves);
   const int64_t waves_total = blocks * kWaves;
   if (n_tiles / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kThreads), lds, stream, a,

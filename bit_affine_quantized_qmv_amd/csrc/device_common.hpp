@@ -79,6 +79,15 @@ struct Fp16 {
   }
 };
 
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS operations, not for
+// its outstanding global/buffer loads (a plain __syncthreads() also drains those, which
+// would stall weight prefetches issued before the barrier).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <class T>
 __device__ inline typename T::v8 as_v8(u32x4 u) {
   return __builtin_bit_cast(typename T::v8, u);
