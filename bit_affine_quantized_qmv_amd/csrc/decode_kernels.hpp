@@ -16,16 +16,18 @@
 namespace qmm {
 namespace decode {
 
-constexpr int kStreamDepth = 6;
 constexpr int kChunkTiles = 2;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kChunkXBytes = 64 * 1024;
 
-template <class T, int BITS, int GS, int MT, int DEPTH>
+template <class T, int BITS, int GS, int MT, int D>
 __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, const int tiles_base,
                                                               const int tiles_rem) {
+  // D = slots per block of the main loop; it divides the slots per tile, so a block never
+  // straddles two tiles and every in-block slot offset is a compile-time constant.
   using S = Slot<BITS, GS>;
   constexpr int MROWS = 16 * MT;
+  constexpr bool kBuf = BITS == 4 || BITS == 8;
   extern __shared__ u32x4 smem[];
   const int K = (int)a.K;
   u32x4* xs = smem;
@@ -33,7 +35,6 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  constexpr bool kBuf = BITS == 4 || BITS == 8;
   // The buffer-descriptor path needs the wave index in a scalar register.  The other code
   // widths keep it per lane: their fp16 instantiations gave run-to-run different results
   // with the scalar form, and that form buys them nothing.
@@ -50,30 +51,24 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
   const int w_voff = col * w_row_bytes + 16 * lg;
   const int sb_voff = col * sb_row_bytes;
 
-  // balanced split of the 16-row tiles over the grid's waves: the first tiles_rem waves take
-  // tiles_base + 1 tiles, the others tiles_base (both computed on the host)
-  const int wid = (int)blockIdx.x * kWaves + wave;
-  const int64_t t_begin = (int64_t)wid * tiles_base + min(wid, tiles_rem);
-  const int64_t t_end = t_begin + tiles_base + (wid < tiles_rem ? 1 : 0);
-  const int nit = K / S::kSpan;
-  const int64_t total = (t_end - t_begin) * nit;
+  // Balanced split of the 16-row tiles over the grid's waves: tiles_rem waves take
+  // tiles_base + 1 tiles, the others tiles_base (both computed on the host).  Ranges are
+  // assigned in the order (wave-in-workgroup, workgroup), so the waves holding an extra tile
+  // are spread over all workgroups (and CUs) instead of packed into the first ones.
+  const int v = wave * (int)gridDim.x + (int)blockIdx.x;
+  const int64_t t_begin = (int64_t)v * tiles_base + min(v, tiles_rem);
+  const int64_t t_end = t_begin + tiles_base + (v < tiles_rem ? 1 : 0);
+  const int nit = K / S::kSpan;              // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
 
   int gword = 0;
   uint32_t gshift = 0;
-  if constexpr (BITS != 4 && BITS != 8) generic_lane_offsets<BITS>(lg, gword, gshift);
+  if constexpr (!kBuf) generic_lane_offsets<BITS>(lg, gword, gshift);
 
-  SlotData<BITS, GS> ring[DEPTH];
-  // Load-stream position: (ld_tile, ld_kit).  After the wave's last slot the stream stays
-  // on that slot (its reloads hit in cache and are never consumed).
-  int64_t ld_tile = t_begin;
-  int ld_kit = 0;
-  // buffer path: per-tile descriptors (rebuilt only when the stream enters a new tile) and
-  // byte offsets of the slot inside the row (advanced by constants)
+  // ---- load stream: block (ld_tile, ld_kb); descriptors rebuilt only on a new tile
   const int64_t w_tile_words = 16 * a.w_row_stride;
   const int64_t sb_tile_elems = 16 * a.sb_row_stride;
   __amdgpu_buffer_rsrc_t w_rs, s_rs, b_rs;
-  int w_soff = 0, sb_soff = 0;
   auto make_tile_rsrc = [&](int64_t tile) {
     const int64_t r0 = tile * 16;
     const int valid = (int)(N - r0 < 16 ? N - r0 : 16);
@@ -81,42 +76,50 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
     s_rs = make_rsrc((const uint16_t*)a.scales + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
     b_rs = make_rsrc((const uint16_t*)a.biases + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
   };
-  if constexpr (kBuf) make_tile_rsrc(t_begin < t_end ? t_begin : 0);
-  auto issue = [&](SlotData<BITS, GS>& d) {
+  int64_t ld_tile = t_begin < t_end ? t_begin : 0;
+  int ld_kb = 0;   // first slot of the block being loaded
+  if constexpr (kBuf) make_tile_rsrc(ld_tile);
+  SlotData<BITS, GS> ring[D];
+  auto issue_slot = [&](int j) {
+    const int kit = ld_kb + j;
     if constexpr (kBuf) {
-      load_slot_buf<BITS, GS>(d, w_rs, s_rs, b_rs, w_voff, w_soff, sb_voff, sb_soff);
+      load_slot_buf<BITS, GS>(ring[j], w_rs, s_rs, b_rs, w_voff, kit * S::kRowWordsPerSlot * 4, sb_voff,
+                              kit * S::kGroups * 2);
     } else {
       const int64_t n = ld_tile * 16 + col;
       const int64_t nl = n < N ? n : N - 1;
-      const uint32_t* wrow = a.w + nl * a.w_row_stride + (int64_t)ld_kit * S::kRowWordsPerSlot;
-      const uint16_t* srow = (const uint16_t*)a.scales + nl * a.sb_row_stride + ld_kit * S::kGroups;
-      const uint16_t* brow = (const uint16_t*)a.biases + nl * a.sb_row_stride + ld_kit * S::kGroups;
-      load_slot<BITS, GS>(d, wrow, srow, brow, lg, gword, row_words - ld_kit * S::kRowWordsPerSlot);
+      load_slot<BITS, GS>(ring[j], a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
+                          (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups,
+                          (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
+                          row_words - kit * S::kRowWordsPerSlot);
     }
-    if (ld_kit + 1 < nit) {
-      ++ld_kit;
-      w_soff += S::kRowWordsPerSlot * 4;
-      sb_soff += S::kGroups * 2;
+  };
+  // move the load stream to the next block.  Past the wave's last block the buffer path
+  // switches to empty descriptors, whose loads return zeros without touching memory; the
+  // pointer path keeps reloading its last block (cache hits).  Neither is ever consumed.
+  auto advance = [&]() {
+    if (ld_kb + D < nit) {
+      ld_kb += D;
     } else if (ld_tile + 1 < t_end) {
       ++ld_tile;
-      ld_kit = 0;
-      w_soff = 0;
-      sb_soff = 0;
+      ld_kb = 0;
       if constexpr (kBuf) make_tile_rsrc(ld_tile);
+    } else if constexpr (kBuf) {
+      w_rs = make_rsrc(a.w, 0u);
+      s_rs = make_rsrc(a.scales, 0u);
+      b_rs = make_rsrc(a.biases, 0u);
     }
   };
 
-  // activations first (their loads must retire before the weight prefetch), then the
-  // prefetch, then the LDS writes of the first staging batch, then any further batches
+  // ---- activations first (their loads must retire before the weight prefetch), then the
+  // first block's loads, then the LDS writes of the first staging batch, then any others
   const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
   const int nbatch = stage_batches<MROWS>(K, kThreads);
   {
     XStage<MROWS> st;
     stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kThreads);
-    // unconditional (no branch may separate these loads from the staging batch's wait); a
-    // wave without tiles loads valid rows it never consumes
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) issue(ring[j]);
+    for (int j = 0; j < D; ++j) issue_slot(j);
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kThreads);
   }
   for (int batch = 1; batch < nbatch; ++batch) {
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
   lds_barrier();
   sum_x<T, GS, MT>(xs, sxs, K, wave, kWaves, lane);
   lds_barrier();
-  if (total == 0) return;
+  if (t_end <= t_begin) return;
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[MT], part[MT];
@@ -136,33 +139,19 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
     acc[mt] = zero4;
     part[mt] = zero4;
   }
-  int64_t cs_tile = t_begin;
-  int cs_kit = 0;
-  auto finish_slot = [&]() {
-    if (++cs_kit == nit) {
-      store_tile<T, MT>(acc, yb, rows, cs_tile * 16 + col, N, lg);
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    for (int kb = 0; kb < nit; kb += D) {
+      // consume the block slot by slot, refilling each slot with the next block's slot
+      advance();
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4;
-      cs_kit = 0;
-      ++cs_tile;
+      for (int j = 0; j < D; ++j) {
+        consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, (kb + j) * S::kSpan, acc, part, lg, col, gshift);
+        issue_slot(j);
+      }
     }
-  };
-
-  const int64_t full = total - total % DEPTH;
-  for (int64_t it = 0; it < full; it += DEPTH) {
+    store_tile<T, MT>(acc, yb, rows, tile * 16 + col, N, lg);
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, cs_kit * S::kSpan, acc, part, lg, col, gshift);
-      issue(ring[j]);
-      finish_slot();
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j) {
-    if (full + j < total) {
-      consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, cs_kit * S::kSpan, acc, part, lg, col, gshift);
-      finish_slot();
-    }
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4;
   }
 }
 
@@ -245,9 +234,9 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
 // ----------------------------------------------------------------------------- launchers
 int device_cus();
 
-template <class T, int BITS, int GS, int MT>
-hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
-  auto kern = qmv_stream_kernel<T, BITS, GS, MT, kStreamDepth>;
+template <class T, int BITS, int GS, int MT, int D>
+hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
+  auto kern = qmv_stream_kernel<T, BITS, GS, MT, D>;
   static int per_cu = -1;  // occupancy for this instantiation (same LDS class each call)
   static int lds_cached = -1;
   if (lds_cached != lds) {
@@ -261,13 +250,29 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
   }
   // one full wave of workgroups (every CU at its occupancy), tiles spread over all waves
   const int64_t n_tiles = (a.N + 15) / 16;
-  const int64_t full = (int64_t)device_cus() * per_cu;
+#ifndef QMM_MAX_WG_PER_CU
+#define QMM_MAX_WG_PER_CU 8
+#endif
+  const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
   const int64_t blocks = std::min<int64_t>(full, (n_tiles + kWaves - 1) / kWaves);
   const int64_t waves_total = blocks * kWaves;
   if (n_tiles / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kThreads), lds, stream, a,
                      (int)(n_tiles / waves_total), (int)(n_tiles % waves_total));
   return hipGetLastError();
+}
+
+// Slots per main-loop block: the largest of 8, 4, 2, 1 dividing the slots per tile.
+template <class T, int BITS, int GS, int MT>
+hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
+  const int nit = (int)(a.K / Slot<BITS, GS>::kSpan);
+#ifndef QMM_MAX_BLOCK_SLOTS
+#define QMM_MAX_BLOCK_SLOTS 4
+#endif
+  if (QMM_MAX_BLOCK_SLOTS >= 8 && nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
+  if (QMM_MAX_BLOCK_SLOTS >= 4 && nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
+  if (nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
+  return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
 }
 
 template <class T, int BITS, int GS, int MT>
