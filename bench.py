@@ -28,6 +28,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+QMV_SOURCES = ["decode.cpp", "decode_b4.hip", "decode_impl.hpp", "decode_kernels.hpp",
+               "device_common.hpp", "kernels.hpp"]
+QMM_T_SOURCES = ["prefill.hip", "device_common.hpp", "kernels.hpp"]
+
+
 def _source_hash(names):
     h = hashlib.sha256()
     for n in names:
@@ -36,36 +41,92 @@ def _source_hash(names):
     return h.hexdigest()[:16]
 
 
-def _traffic(summary_name, kernel_sources, launches_per_dispatch=1):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on
-    the current kernel source (else None)."""
+def _traffic(summary_name, kernel_sources):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary (a line
+    'traffic-json: {...}' in profiles/<summary_name>), if its counters were taken on the
+    current kernel source; else None."""
     path = os.path.join(PROFILES, summary_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_hash") != _source_hash(kernel_sources):
-        return None
-    return d.get("hbm_bytes_per_launch")
+        for ln in f:
+            if ln.startswith("traffic-json:"):
+                d = json.loads(ln.split(":", 1)[1])
+                if d.get("source_hash") != _source_hash(kernel_sources):
+                    return None
+                return d.get("hbm_bytes_per_launch")
+    return None
 
 
-def _time_kernel(fn, steps, warmup, torch):
-    """Run fn(i) warmup + steps times; returns (wall ms per step, mean kernel ms)."""
+def _time_steps(fn, steps, warmup, torch, use_graph=True):
+    """Times `steps` calls of fn(i) three ways:
+
+    wall_ms    -- the steps captured once into a HIP graph, whose replay is bracketed by
+                  torch.cuda.synchronize() on both sides (host wall clock per step);
+    kernel_ms  -- the same steps launched eagerly behind a sleep kernel, so the queue stays
+                  ahead of the host, with an event pair around every launch on the launch
+                  stream (mean / median / p10 / p90 of the per-launch durations);
+    eager_ms   -- the steps launched eagerly from Python with synchronize on both sides
+                  (includes the host's per-call marshalling; context only).
+    """
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
     t0 = time.perf_counter()
     for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    graph_ok = use_graph
+    try:
+        if not use_graph:
+            raise RuntimeError("graph timing disabled")
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)                      # launch-side caches are filled outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        del g
+    except Exception:              # timing only: report the eager figure instead
+        graph_ok = False
+        wall_ms = eager_ms
+
+    # queue primed with a sleep kernel long enough to cover the host's enqueue time
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(1_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    host_ms = 3.0 * eager_ms * steps + 5.0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda._sleep(int(cycles_per_ms * host_ms))
+    for i in range(steps):
         starts[i].record()
-        fn(warmup + i)
+        fn(i)
         ends[i].record()
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kern.sort()
-    return wall_ms, sum(kern) / len(kern), kern[len(kern) // 2]
+    kern = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    span_ms = starts[0].elapsed_time(ends[-1]) / steps
+    q = lambda f: kern[min(len(kern) - 1, int(f * len(kern)))]
+    return {"wall_ms": wall_ms, "graph": graph_ok, "eager_ms": eager_ms,
+            "queued_span_ms": span_ms, "kernel_mean_ms": sum(kern) / len(kern),
+            "kernel_median_ms": q(0.5), "kernel_p10_ms": q(0.1), "kernel_p90_ms": q(0.9)}
 
 
 def _cpu_threads():
@@ -100,6 +161,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing per leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["qmv", "qmm_t", "all"], default="all")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps eagerly instead of replaying them from a HIP graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -112,8 +177,17 @@ def main():
     import bit_affine_quantized_qmv_amd as q
     import synth
 
-    q.load()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": src.numel() * 4,
+                          "bytes_written": dst.numel() * 4, "launches": 5}))
+        return
+    q.load()
     out = {}
 
     # ------------------------------------------------------------ lm_head decode qmv
@@ -129,12 +203,13 @@ def main():
     xs = [x0.clone() for _ in range(copies)]
     ys = [torch.empty(m, 1, n, dtype=x0.dtype, device=dev) for _ in range(copies)]
     qmv_bytes = n * k * bits // 8 + 2 * n * (k // gs) * 2 + m * k * 2 + m * n * 2
-    wall, kern_mean, kern_med = _time_kernel(
-        lambda i: q.qmv(xs[i % copies], qws[i % copies], out=ys[i % copies]), args.steps, args.warmup, torch)
-    forced = _time_kernel(lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED,
-                                          out=ys[i % copies]), max(5, args.steps // 10), 3, torch)
-    qmv_value = qmv_bytes / (wall * 1e-3) / 1e9
-    achieved = qmv_bytes / (kern_mean * 1e-3) / 1e9
+    t = _time_steps(lambda i: q.qmv(xs[i % copies], qws[i % copies], out=ys[i % copies]),
+                    args.steps, args.warmup, torch, not args.no_graph)
+    tf = _time_steps(lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED,
+                                     out=ys[i % copies]), max(10, args.steps // 4), 3, torch,
+                    not args.no_graph)
+    qmv_value = qmv_bytes / (t["wall_ms"] * 1e-3) / 1e9
+    achieved = qmv_bytes / (t["kernel_mean_ms"] * 1e-3) / 1e9
     line = {
         "metric": "qmv effective HBM GB/s (lm_head decode)",
         "value": round(qmv_value, 1),
@@ -142,7 +217,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall, 5),
+        "ms_per_step": round(t["wall_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -151,15 +226,19 @@ def main():
         "config": {"workload": "lm_head decode qmv: x [32,1,1024] bf16, W [151936,1024] 4-bit "
                                "group 64 bf16 scales/biases, folded to one 2D call",
                    "algorithmic_bytes_per_call": qmv_bytes, "weight_copies_rotated": copies,
+                   "timing": "K steps captured in one HIP graph, replay bracketed by synchronize"
+                             if t["graph"] else "K eager steps bracketed by synchronize",
                    "pct_hbm_peak": round(100 * qmv_value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("qmv_lm_head_traffic.json",
-                                         ["decode.hip", "device_common.hpp"]),
-                     "kernel": "qmv_decode_kernel", "kernel_ms_mean": round(kern_mean, 5),
-                     "kernel_ms_median": round(kern_med, 5)},
-        "context": {"forced_per_batch_element_ms": round(forced[1], 4),
-                    "forced_vs_folded": round(forced[1] / kern_mean, 2),
+                     "traffic": _traffic("qmv_stream_kernel_lm_head_traffic.md", QMV_SOURCES),
+                     "kernel": "qmv_stream_kernel",
+                     "kernel_ms_mean": round(t["kernel_mean_ms"], 5),
+                     "kernel_ms_median": round(t["kernel_median_ms"], 5),
+                     "kernel_ms_p10_p90": [round(t["kernel_p10_ms"], 5), round(t["kernel_p90_ms"], 5)]},
+        "context": {"eager_python_ms_per_step": round(t["eager_ms"], 5),
+                    "forced_strided_32x1_kernel_ms": round(tf["kernel_mean_ms"], 5),
+                    "forced_vs_folded": round(tf["kernel_mean_ms"] / t["kernel_mean_ms"], 2),
                     "pages_apple_m4max_ms": {"batched_grid_z": 60.0, "flattened": 2.2}},
     }
     out["qmv"] = line
@@ -180,28 +259,26 @@ def main():
         pys = [torch.empty(bb, ss, pn, dtype=px0.dtype, device=dev) for _ in range(pcopies)]
         flops = 2.0 * bb * ss * pn * pk
         psteps = max(10, args.steps // 4)
-        pwall, pk_mean, pk_med = _time_kernel(
-            lambda i: q.qmm_t(pxs[i % pcopies], pqs[i % pcopies], out=pys[i % pcopies]), psteps,
-            max(3, args.warmup // 4), torch)
+        pt = _time_steps(lambda i: q.qmm_t(pxs[i % pcopies], pqs[i % pcopies], out=pys[i % pcopies]),
+                         psteps, max(3, args.warmup // 4), torch, not args.no_graph)
         buf = synth.normal_x((bb, 2 * ss, pk), pc["dtype"], seed=pc["buf_seed"]).to(dev)
         view = buf[:, 0:ss, :]
-        vwall, vk_mean, _ = _time_kernel(lambda i: q.qmm_t(view, pqs[i % pcopies], out=pys[i % pcopies]),
-                                         max(5, psteps // 2), 2, torch)
-        tflops = flops / (pwall * 1e-3) / 1e12
-        ach = flops / (pk_mean * 1e-3) / 1e12
+        pv = _time_steps(lambda i: q.qmm_t(view, pqs[i % pcopies], out=pys[i % pcopies]),
+                         max(5, psteps // 2), 2, torch, not args.no_graph)
+        tflops = flops / (pt["wall_ms"] * 1e-3) / 1e12
+        ach = flops / (pt["kernel_mean_ms"] * 1e-3) / 1e12
         out["qmm_t"] = {
             "metric": "qmm_t TFLOP/s (prefill)", "value": round(tflops, 1), "unit": "TFLOP/s",
-            "steps": psteps, "ms_per_step": round(pwall, 5), "dtype": "bf16",
+            "steps": psteps, "ms_per_step": round(pt["wall_ms"], 5), "dtype": "bf16",
             "config": {"workload": "prefill qmm_t: x [4,512,4096] bf16, W [14336,4096] 4-bit group 128 "
                                    "bf16 scales/biases, y [4,512,14336]",
                        "flops_per_call": flops, "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
-                       "narrowed_view_kernel_ms": round(vk_mean, 5)},
+                       "narrowed_view_kernel_ms": round(pv["kernel_mean_ms"], 5)},
             "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": _traffic("qmm_t_prefill_traffic.json",
-                                             ["prefill.hip", "device_common.hpp"]),
-                         "kernel": "qmm_prefill_kernel", "kernel_ms_mean": round(pk_mean, 5),
-                         "kernel_ms_median": round(pk_med, 5)},
+                         "traffic": _traffic("qmm_prefill_kernel_prefill_traffic.md", QMM_T_SOURCES),
+                         "kernel": "qmm_prefill_kernel", "kernel_ms_mean": round(pt["kernel_mean_ms"], 5),
+                         "kernel_ms_median": round(pt["kernel_median_ms"], 5)},
         }
         del pqs, pxs, pys, buf, pw
 
