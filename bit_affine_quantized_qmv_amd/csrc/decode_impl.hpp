@@ -8,9 +8,12 @@
 // property transformers issue 47331 asks for under "Expected behavior"):
 //   * sum_{k in g} x q   : chain of 16x16x32 MFMAs over the group's 32-k steps, codes given
 //                          as exact bf16/fp16 integers, fresh accumulator per group;
+//   * acc = fma(s, sum xq, acc), group by group in k order;
 //   * sum_{k in g} x     : the same MFMA chain against an all-ones operand (each x widened
-//                          by the matrix core, accumulated in float32);
-//   * acc = fma(s, sum xq, acc); acc = fma(b, sum x, acc), group by group in k order;
+//                          by the matrix core, accumulated in float32), once per call;
+//   * after the scale updates of one weight slot (1, 2 or 4 groups), the slot's bias terms
+//     b * sum x in one float32 16x16x4 MFMA whose k index is the group (unused k lanes
+//     carry b = 0), accumulated into acc;
 //   * one round-to-nearest-even to the output dtype.
 // Activation rows past the call's row count are zero in LDS; weight rows past N are read
 // as row N-1 (or as zeros, through a range-checked buffer descriptor) and never stored
@@ -68,36 +71,72 @@ struct Slot {
   static constexpr int kRowWordsPerSlot = kSpan * BITS / 32;
 };
 
-template <int N>
-struct SbRegs;  // scale or bias values of the groups in a slot, raw 16-bit patterns
-template <>
-struct SbRegs<1> { uint16_t v; __device__ uint32_t get(int) const { return v; } };
-template <>
-struct SbRegs<2> { uint32_t v; __device__ uint32_t get(int i) const { return (v >> (16 * i)) & 0xFFFFu; } };
-template <>
-struct SbRegs<4> {
-  uint32_t v0, v1;
-  __device__ uint32_t get(int i) const { return ((i < 2 ? v0 : v1) >> (16 * (i & 1))) & 0xFFFFu; }
+// Scale or bias values (raw 16-bit patterns) of NH consecutive groups of one weight row,
+// two per register.  get(h): halfword h (compile-time h).  lane_half<KG>(base, lg): the
+// value a lane feeds as k index lg of a bias MFMA covering the KG groups starting at
+// halfword `base`; 0 for lg >= KG.
+template <int NH>
+struct SbRegs {
+  uint32_t v[(NH + 1) / 2];
+  __device__ uint32_t get(int h) const { return (v[h >> 1] >> (16 * (h & 1))) & 0xFFFFu; }
+  template <int KG>
+  __device__ uint32_t lane_half(int base, int lg) const {
+    if constexpr (KG == 1) {
+      return lg == 0 ? get(base) : 0u;
+    } else if constexpr (KG == 2) {   // base is even
+      return lg < 2 ? (v[base >> 1] >> (16 * lg)) & 0xFFFFu : 0u;
+    } else {                          // KG == 4, base a multiple of 4
+      const uint32_t w = (lg & 2) ? v[(base >> 1) + 1] : v[base >> 1];
+      return (w >> (16 * (lg & 1))) & 0xFFFFu;
+    }
+  }
 };
 
 template <int N>
 __device__ inline SbRegs<N> load_sb(const uint16_t* p) {
   SbRegs<N> r;
   if constexpr (N == 1) {
-    r.v = *p;
+    r.v[0] = *p;
   } else if constexpr (N == 2) {
-    r.v = *(const uint32_t*)p;
+    r.v[0] = *(const uint32_t*)p;
   } else {
     const uint2 u = *(const uint2*)p;
-    r.v0 = u.x;
-    r.v1 = u.y;
+    r.v[0] = u.x;
+    r.v[1] = u.y;
   }
   return r;
 }
 
+// NH halfwords at byte offset voff + soff of a buffer, NH * 2 in {2, 4, 8} bytes or a
+// multiple of 16 (the offset is aligned to the load width).
+template <int NH>
+__device__ inline void load_sb_buf(SbRegs<NH>& r, __amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  if constexpr (NH == 1) {
+    r.v[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
+  } else if constexpr (NH == 2) {
+    r.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  } else if constexpr (NH == 4) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    r.v[0] = u[0];
+    r.v[1] = u[1];
+  } else {
+    static_assert(NH % 8 == 0, "scale/bias block loads are 2, 4, 8 or 16*k bytes");
+#pragma unroll
+    for (int i = 0; i < NH / 8; ++i) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, 0);
+      r.v[4 * i + 0] = u[0];
+      r.v[4 * i + 1] = u[1];
+      r.v[4 * i + 2] = u[2];
+      r.v[4 * i + 3] = u[3];
+    }
+  }
+}
+
 template <int BITS, int GS>
 struct SlotData {
-  uint32_t w[Slot<BITS, GS>::kWords];
+  static constexpr bool kVecCodes = BITS == 4 || BITS == 8;
+  u32x4 v[kVecCodes ? Slot<BITS, GS>::kVec : 1];          // 4/8-bit codes, 16-byte loads as issued
+  uint32_t w[kVecCodes ? 1 : Slot<BITS, GS>::kWords];     // other widths
   SbRegs<Slot<BITS, GS>::kGroups> s, b;
 };
 
@@ -109,13 +148,7 @@ __device__ inline void load_slot(SlotData<BITS, GS>& d, const uint32_t* wrow, co
   using S = Slot<BITS, GS>;
   if constexpr (BITS == 4 || BITS == 8) {
 #pragma unroll
-    for (int v = 0; v < S::kVec; ++v) {
-      const u32x4 u = *(const u32x4*)(wrow + 16 * v + 4 * lg);
-      d.w[4 * v + 0] = u.x;
-      d.w[4 * v + 1] = u.y;
-      d.w[4 * v + 2] = u.z;
-      d.w[4 * v + 3] = u.w;
-    }
+    for (int v = 0; v < S::kVec; ++v) d.v[v] = *(const u32x4*)(wrow + 16 * v + 4 * lg);
   } else {
 #pragma unroll
     for (int c = 0; c < S::kSteps; ++c) {
@@ -129,10 +162,11 @@ __device__ inline void load_slot(SlotData<BITS, GS>& d, const uint32_t* wrow, co
   d.b = load_sb<S::kGroups>(brow);
 }
 
-// Buffer-descriptor variant of load_slot: `w_rs`, `s_rs`, `b_rs` describe one 16-row tile
-// (rows past N lie outside the descriptor's range and read as zero); the lane's row offset
-// is in `w_voff` / `sb_voff` (bytes), the slot's offset inside the row in `w_soff` / `sb_soff`.
-template <int BITS, int GS>
+// Buffer-descriptor variant of load_slot: `w_rs`, `s_rs`, `b_rs` describe the rows of a
+// tile pair (rows outside the range read as zero); the lane's row offset is in `w_voff` /
+// `sb_voff` (bytes), the slot's offset inside the row in `w_soff` / `sb_soff`.  With
+// WITH_SB false the scales and biases are loaded per block elsewhere.
+template <int BITS, int GS, bool WITH_SB>
 __device__ inline void load_slot_buf(SlotData<BITS, GS>& d, __amdgpu_buffer_rsrc_t w_rs,
                                      __amdgpu_buffer_rsrc_t s_rs, __amdgpu_buffer_rsrc_t b_rs, int w_voff,
                                      int w_soff, int sb_voff, int sb_soff) {
@@ -141,24 +175,11 @@ __device__ inline void load_slot_buf(SlotData<BITS, GS>& d, __amdgpu_buffer_rsrc
 #pragma unroll
   for (int v = 0; v < S::kVec; ++v) {
     const auto u = __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_voff + 64 * v, w_soff, 0);
-    d.w[4 * v + 0] = u[0];
-    d.w[4 * v + 1] = u[1];
-    d.w[4 * v + 2] = u[2];
-    d.w[4 * v + 3] = u[3];
+    d.v[v] = u32x4{u[0], u[1], u[2], u[3]};
   }
-  if constexpr (S::kGroups == 1) {
-    d.s.v = __builtin_amdgcn_raw_buffer_load_b16(s_rs, sb_voff, sb_soff, 0);
-    d.b.v = __builtin_amdgcn_raw_buffer_load_b16(b_rs, sb_voff, sb_soff, 0);
-  } else if constexpr (S::kGroups == 2) {
-    d.s.v = __builtin_amdgcn_raw_buffer_load_b32(s_rs, sb_voff, sb_soff, 0);
-    d.b.v = __builtin_amdgcn_raw_buffer_load_b32(b_rs, sb_voff, sb_soff, 0);
-  } else {
-    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(s_rs, sb_voff, sb_soff, 0);
-    const auto bv = __builtin_amdgcn_raw_buffer_load_b64(b_rs, sb_voff, sb_soff, 0);
-    d.s.v0 = sv[0];
-    d.s.v1 = sv[1];
-    d.b.v0 = bv[0];
-    d.b.v1 = bv[1];
+  if constexpr (WITH_SB) {
+    load_sb_buf<S::kGroups>(d.s, s_rs, sb_voff, sb_soff);
+    load_sb_buf<S::kGroups>(d.b, b_rs, sb_voff, sb_soff);
   }
 }
 
@@ -167,34 +188,37 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Exact code values of MFMA step c of a slot, in operand order.
-template <class T, int BITS, int GS>
-__device__ inline u32x4 slot_codes(const SlotData<BITS, GS>& d, int c, uint32_t generic_shift) {
-  if constexpr (BITS == 4) {
-    return codes4_to_v8<T>(d.w[c]);
-  } else if constexpr (BITS == 8) {
-    const int v = c >> 1;
-    return (c & 1) ? codes8_to_v8<T>(d.w[4 * v + 2], d.w[4 * v + 3])
-                   : codes8_to_v8<T>(d.w[4 * v + 0], d.w[4 * v + 1]);
-  } else {
-    return codesN_to_v8<T, BITS>(d.w[2 * c], d.w[2 * c + 1], generic_shift);
-  }
-}
-
-// Cross-lane reordering that follows the loads (done right before use).
+// Codes of one slot after the cross-lane reordering that follows the loads: 4-bit words
+// transposed across lane groups, 8-bit halves swapped; other widths unchanged.  The ring
+// registers themselves are never rewritten, so a refill can target them directly.
 template <int BITS, int GS>
-__device__ inline void slot_reorder(SlotData<BITS, GS>& d) {
+struct SlotCodes {
+  u32x4 v[SlotData<BITS, GS>::kVecCodes ? Slot<BITS, GS>::kVec : 1];
+};
+
+template <int BITS, int GS>
+__device__ inline SlotCodes<BITS, GS> slot_reorder(const SlotData<BITS, GS>& d) {
+  SlotCodes<BITS, GS> r;
   if constexpr (BITS == 4) {
-    u32x4 u = {d.w[0], d.w[1], d.w[2], d.w[3]};
-    u = transpose_lane_groups(u);
-    d.w[0] = u.x; d.w[1] = u.y; d.w[2] = u.z; d.w[3] = u.w;
+    r.v[0] = transpose_lane_groups(d.v[0]);
   } else if constexpr (BITS == 8) {
 #pragma unroll
-    for (int v = 0; v < Slot<BITS, GS>::kVec; ++v) {
-      u32x4 u = {d.w[4 * v], d.w[4 * v + 1], d.w[4 * v + 2], d.w[4 * v + 3]};
-      u = swap_halves(u);
-      d.w[4 * v] = u.x; d.w[4 * v + 1] = u.y; d.w[4 * v + 2] = u.z; d.w[4 * v + 3] = u.w;
-    }
+    for (int v = 0; v < Slot<BITS, GS>::kVec; ++v) r.v[v] = swap_halves(d.v[v]);
+  }
+  return r;
+}
+
+// Exact code values of MFMA step c of a slot, in operand order.
+template <class T, int BITS, int GS>
+__device__ inline u32x4 slot_codes(const SlotData<BITS, GS>& d, const SlotCodes<BITS, GS>& r, int c,
+                                   uint32_t generic_shift) {
+  if constexpr (BITS == 4) {
+    return codes4_to_v8<T>(r.v[0][c]);
+  } else if constexpr (BITS == 8) {
+    const int v = c >> 1;
+    return (c & 1) ? codes8_to_v8<T>(r.v[v].z, r.v[v].w) : codes8_to_v8<T>(r.v[v].x, r.v[v].y);
+  } else {
+    return codesN_to_v8<T, BITS>(d.w[2 * c], d.w[2 * c + 1], generic_shift);
   }
 }
 
@@ -227,7 +251,10 @@ template <class T, int BITS, int MROWS>
 __device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb, int rows, int tid) {
   const int m = tid % MROWS;
   const int mr = m < rows ? m : 0;   // rows past the call's rows read row 0, stored as zero
-  return xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride;
+  // decode calls have at most 32 rows, so the segment arithmetic fits 32-bit integers
+  const uint32_t sr = a.seg_rows < MROWS ? (uint32_t)a.seg_rows : (uint32_t)MROWS;
+  const uint32_t seg = (uint32_t)mr / sr;
+  return xb + (int64_t)seg * a.seg_stride + (int64_t)((uint32_t)mr - seg * sr) * a.row_stride;
 }
 
 template <class T, int BITS, int MROWS>
@@ -284,7 +311,17 @@ __device__ inline void stage_x(u32x4* xs, const MatArgs& a, const uint16_t* xb, 
 }
 
 // Per (row, group) sums of the staged activations: MFMA against an all-ones operand, one
-// chain per (16-row tile, group), shared out over the workgroup's waves.
+// chain per (16-row tile, group), shared out over the workgroup's waves.  Layout
+// sxs[g * MROWS + m]; callers keep kSxPad zero groups after the last one, which the bias
+// MFMA of the final slot reads on its unused k lanes.
+constexpr int kSxPad = 3;
+
+template <int MT>
+__device__ inline void zero_sx_pad(float* sxs, int ng, int tid) {
+  constexpr int MROWS = 16 * MT;
+  if (tid < kSxPad * MROWS) sxs[ng * MROWS + tid] = 0.f;
+}
+
 template <class T, int GS, int MT>
 __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, int nwaves, int lane) {
   constexpr int MROWS = 16 * MT;
@@ -293,6 +330,7 @@ __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, i
   const int ng = k_len / GS;
   const uint32_t one2 = T::pack2(1.0f, 1.0f);
   const u32x4 ones = {one2, one2, one2, one2};
+#pragma unroll 4
   for (int p = wave; p < MT * ng; p += nwaves) {
     const int mt = p / ng, g = p - mt * ng;
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -303,41 +341,60 @@ __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, i
   }
 }
 
-// Consume one slot: MFMAs of its steps, and the scale/bias update at each group end.
-// k_local = k offset of the slot inside the staged activation chunk.
-template <class T, int BITS, int GS, int MT>
-__device__ inline void consume_slot(SlotData<BITS, GS>& d, const u32x4* xs, const float* sxs, int k_local,
-                                    f32x4 (&acc)[MT], f32x4 (&part)[MT], int lg, int col,
+// Consume one slot of TN 16-row weight tiles: MFMAs of its steps (each activation operand
+// read from LDS once and used for every tile), the scale update at each group end, then the
+// slot's bias terms on the float32 matrix core.  k_local = k offset of the slot inside the
+// staged activation chunk.
+// Scales and biases come from `sc` / `bi` (NH halfwords per tile), the slot's groups
+// starting at halfword `hbase`.
+template <class T, int BITS, int GS, int MT, int TN, int NH>
+__device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbRegs<NH> (&sc)[TN],
+                                    const SbRegs<NH> (&bi)[TN], int hbase, const u32x4* xs, const float* sxs,
+                                    int k_local, f32x4 (&acc)[TN][MT], f32x4 (&part)[TN][MT], int lg, int col,
                                     uint32_t generic_shift) {
   using S = Slot<BITS, GS>;
   constexpr int MROWS = 16 * MT;
   constexpr int SPG = GS / 32;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  slot_reorder<BITS, GS>(d);
+  SlotCodes<BITS, GS> rc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) rc[t] = slot_reorder<BITS, GS>(d[t]);
   const int step0 = k_local >> 5;
 #pragma unroll
   for (int c = 0; c < S::kSteps; ++c) {
-    const typename T::v8 bq = as_v8<T>(slot_codes<T, BITS, GS>(d, c, generic_shift));
+    typename T::v8 bq[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) bq[t] = as_v8<T>(slot_codes<T, BITS, GS>(d[t], rc[t], c, generic_shift));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const typename T::v8 av = as_v8<T>(xs[((step0 + c) * 4 + lg) * MROWS + mt * 16 + col]);
-      part[mt] = T::mfma(av, bq, (c % SPG) == 0 ? zero4 : part[mt]);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) part[t][mt] = T::mfma(av, bq[t], (c % SPG) == 0 ? zero4 : part[t][mt]);
     }
     if ((c + 1) % SPG == 0) {
       const int gi = c / SPG;
-      const float sv = T::to_f32(d.s.get(gi));
-      const float bv = T::to_f32(d.b.get(gi));
-      const int gl = k_local / GS + gi;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 sx = *(const f32x4*)&sxs[gl * MROWS + mt * 16 + 4 * lg];
+      for (int t = 0; t < TN; ++t) {
+        const float sv = T::to_f32(sc[t].get(hbase + gi));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[mt][r] = __builtin_fmaf(sv, part[mt][r], acc[mt][r]);
-          acc[mt][r] = __builtin_fmaf(bv, sx[r], acc[mt][r]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][mt][r] = __builtin_fmaf(sv, part[t][mt][r], acc[t][mt][r]);
       }
     }
+  }
+  // bias terms: A[m][k] = sum x of row m in group g0 + k, B[k][n] = b[n][g0 + k]; the k lanes
+  // past the slot's groups carry b = 0 (their A values are the next groups' sums or the zero
+  // padding, finite either way)
+  const int g0 = k_local / GS;
+  float sxa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) sxa[mt] = sxs[(g0 + lg) * MROWS + mt * 16 + col];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const float bv = T::to_f32(bi[t].template lane_half<S::kGroups>(hbase, lg));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[mt], bv, acc[t][mt], 0, 0, 0);
   }
 }
 
@@ -352,6 +409,33 @@ __device__ inline void store_tile(const f32x4 (&acc)[MT], uint16_t* yb, int rows
       const int m = mt * 16 + 4 * lg + r;
       if (m < rows) yb[(int64_t)m * N + n] = T::from_f32(acc[mt][r]);
     }
+}
+
+// Store of a full tile pair through a per-wave LDS area (MROWS rows of kYRow halfwords):
+// the lanes write their fragment values, then each lane stores MROWS bytes of one output
+// row with 16-byte stores.  Needs 16-byte aligned output rows.  The area is private to the
+// wave, whose LDS operations complete in order, so no barrier is involved.
+constexpr int kYRow = 40;   // 32 values of a row + 8 halfwords of padding (80 bytes)
+
+template <class T, int MT, int TN>
+__device__ inline void store_pair_lds(const f32x4 (&acc)[TN][MT], uint16_t* ys, uint16_t* yb, int rows, int64_t n0,
+                                      int64_t N, int lane, int lg, int col) {
+  static_assert(TN == 2, "a pair is 32 output columns");
+  constexpr int MROWS = 16 * MT;
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[(mt * 16 + 4 * lg + r) * kYRow + t * 16 + col] = T::from_f32(acc[t][mt][r]);
+  constexpr int kPer = MROWS / 16;          // 16-byte pieces per lane (a row holds 4 pieces)
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int piece = lane * kPer + i;      // row piece / 4, column block piece % 4
+    const int m = piece >> 2, qd = piece & 3;
+    const u32x4 v = *(const u32x4*)(ys + m * kYRow + qd * 8);
+    if (m < rows) *(u32x4*)(yb + (int64_t)m * N + n0 + qd * 8) = v;
+  }
 }
 
 }  // namespace decode

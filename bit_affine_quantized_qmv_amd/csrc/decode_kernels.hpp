@@ -20,14 +20,36 @@ constexpr int kChunkTiles = 2;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kChunkXBytes = 64 * 1024;
 
-template <class T, int BITS, int GS, int MT, int D>
-__global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, const int tiles_base,
-                                                              const int tiles_rem) {
-  // D = slots per block of the main loop; it divides the slots per tile, so a block never
-  // straddles two tiles and every in-block slot offset is a compile-time constant.
+#ifndef QMM_STREAM_WAVES
+#define QMM_STREAM_WAVES 8
+#endif
+#ifndef QMM_STREAM_MIN_WG
+#define QMM_STREAM_MIN_WG 2
+#endif
+constexpr int kStreamWaves = QMM_STREAM_WAVES;
+constexpr int kStreamThreads = 64 * kStreamWaves;
+constexpr int kPair = 2;   // weight tiles consumed together per slot
+#ifndef QMM_Y_LDS
+#define QMM_Y_LDS 0
+#endif
+constexpr bool kYLds = QMM_Y_LDS != 0;   // full tile pairs stored through LDS
+
+template <class T, int BITS, int GS, int MT, int D, bool SBB>
+__global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_kernel(const MatArgs a,
+                                                                                     const int tiles_base,
+                                                                                     const int tiles_rem) {
+  // The slots of a wave's tile pairs form one stream, consumed in sub-blocks of D slots (D
+  // divides the slots per tile, so a pair always ends on a sub-block boundary).  Weight
+  // loads run 2*D slots ahead of consumption (a ring of 2*D slots); with SBB the scales and
+  // biases are loaded once per sub-block, one vector load per tile row, D slots ahead, into
+  // two register sets used by alternate sub-blocks; without it each slot carries its own.
   using S = Slot<BITS, GS>;
   constexpr int MROWS = 16 * MT;
+  constexpr int TN = kPair;
+  constexpr int R = 2 * D;
   constexpr bool kBuf = BITS == 4 || BITS == 8;
+  static_assert(!SBB || kBuf, "block scale/bias loads use the buffer path");
+  constexpr int NHB = D * S::kGroups;   // scale (or bias) halfwords per tile row per sub-block
   extern __shared__ u32x4 smem[];
   const int K = (int)a.K;
   u32x4* xs = smem;
@@ -48,110 +70,198 @@ __global__ __launch_bounds__(kThreads) void qmv_stream_kernel(const MatArgs a, c
   uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
   const int w_row_bytes = (int)(a.w_row_stride * 4);
   const int sb_row_bytes = (int)(a.sb_row_stride * 2);
-  const int w_voff = col * w_row_bytes + 16 * lg;
-  const int sb_voff = col * sb_row_bytes;
+  int w_voff[TN], sb_voff[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    w_voff[t] = (16 * t + col) * w_row_bytes + 16 * lg;
+    sb_voff[t] = (16 * t + col) * sb_row_bytes;
+  }
 
   // Balanced split of the 16-row tiles over the grid's waves: tiles_rem waves take
   // tiles_base + 1 tiles, the others tiles_base (both computed on the host).  Ranges are
   // assigned in the order (wave-in-workgroup, workgroup), so the waves holding an extra tile
-  // are spread over all workgroups (and CUs) instead of packed into the first ones.
+  // are spread over all workgroups (and CUs).  A wave walks its range two tiles at a time;
+  // when the range is odd, the last pair's second tile is empty (zero loads, no store).
   const int v = wave * (int)gridDim.x + (int)blockIdx.x;
   const int64_t t_begin = (int64_t)v * tiles_base + min(v, tiles_rem);
   const int64_t t_end = t_begin + tiles_base + (v < tiles_rem ? 1 : 0);
   const int nit = K / S::kSpan;              // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
+  uint16_t* ys = (uint16_t*)(sxs + (K / GS + kSxPad) * MROWS) + wave * MROWS * kYRow;
+  const bool y_vec = (N & 7) == 0 && ((uintptr_t)yb & 15) == 0;
 
   int gword = 0;
   uint32_t gshift = 0;
   if constexpr (!kBuf) generic_lane_offsets<BITS>(lg, gword, gshift);
 
-  // ---- load stream: block (ld_tile, ld_kb); descriptors rebuilt only on a new tile
-  const int64_t w_tile_words = 16 * a.w_row_stride;
-  const int64_t sb_tile_elems = 16 * a.sb_row_stride;
-  __amdgpu_buffer_rsrc_t w_rs, s_rs, b_rs;
-  auto make_tile_rsrc = [&](int64_t tile) {
-    const int64_t r0 = tile * 16;
-    const int valid = (int)(N - r0 < 16 ? N - r0 : 16);
-    w_rs = make_rsrc(a.w + tile * w_tile_words, (uint32_t)(valid * w_row_bytes));
-    s_rs = make_rsrc((const uint16_t*)a.scales + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
-    b_rs = make_rsrc((const uint16_t*)a.biases + tile * sb_tile_elems, (uint32_t)(valid * sb_row_bytes));
+  // Descriptors over the rows of tile pair p that lie in [0, N) and in the wave's range;
+  // past the range they are empty (loads return zero without touching memory).
+  auto rows_valid = [&](int64_t p) -> uint32_t {
+    if (p >= t_end) return 0u;
+    int64_t valid = N - p * 16 < 16 * TN ? N - p * 16 : 16 * TN;
+    valid = valid < (t_end - p) * 16 ? valid : (t_end - p) * 16;
+    return (uint32_t)valid;
   };
-  int64_t ld_tile = t_begin < t_end ? t_begin : 0;
-  int ld_kb = 0;   // first slot of the block being loaded
-  if constexpr (kBuf) make_tile_rsrc(ld_tile);
-  SlotData<BITS, GS> ring[D];
-  auto issue_slot = [&](int j) {
-    const int kit = ld_kb + j;
-    if constexpr (kBuf) {
-      load_slot_buf<BITS, GS>(ring[j], w_rs, s_rs, b_rs, w_voff, kit * S::kRowWordsPerSlot * 4, sb_voff,
-                              kit * S::kGroups * 2);
-    } else {
-      const int64_t n = ld_tile * 16 + col;
-      const int64_t nl = n < N ? n : N - 1;
-      load_slot<BITS, GS>(ring[j], a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
-                          (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups,
-                          (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
-                          row_words - kit * S::kRowWordsPerSlot);
+  auto w_rsrc = [&](int64_t p) { return make_rsrc(a.w + p * 16 * a.w_row_stride, rows_valid(p) * w_row_bytes); };
+  auto s_rsrc = [&](int64_t p) {
+    return make_rsrc((const uint16_t*)a.scales + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes);
+  };
+  auto b_rsrc = [&](int64_t p) {
+    return make_rsrc((const uint16_t*)a.biases + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes);
+  };
+
+  // ---- weight stream: next sub-block to load is slots [w_kb, w_kb + D) of pair w_p
+  int64_t w_p = t_begin;
+  int w_kb = 0;
+  __amdgpu_buffer_rsrc_t w_rs, ws_rs, wb_rs;
+  if constexpr (kBuf) {
+    w_rs = w_rsrc(w_p);
+    if constexpr (!SBB) {
+      ws_rs = s_rsrc(w_p);
+      wb_rs = b_rsrc(w_p);
+    }
+  }
+  SlotData<BITS, GS> ring[R][TN];
+  auto issue_w = [&](int j, int r) {
+    const int kit = w_kb + j;
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      if constexpr (kBuf) {
+        load_slot_buf<BITS, GS, !SBB>(ring[r][t], w_rs, ws_rs, wb_rs, w_voff[t], kit * S::kRowWordsPerSlot * 4,
+                                      sb_voff[t], kit * S::kGroups * 2);
+      } else {
+        const int64_t n = w_p * 16 + 16 * t + col;
+        const int64_t nl = n < N ? n : N - 1;
+        load_slot<BITS, GS>(ring[r][t], a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
+                            (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups,
+                            (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
+                            row_words - kit * S::kRowWordsPerSlot);
+      }
     }
   };
-  // move the load stream to the next block.  Past the wave's last block the buffer path
-  // switches to empty descriptors, whose loads return zeros without touching memory; the
-  // pointer path keeps reloading its last block (cache hits).  Neither is ever consumed.
-  auto advance = [&]() {
-    if (ld_kb + D < nit) {
-      ld_kb += D;
-    } else if (ld_tile + 1 < t_end) {
-      ++ld_tile;
-      ld_kb = 0;
-      if constexpr (kBuf) make_tile_rsrc(ld_tile);
-    } else if constexpr (kBuf) {
-      w_rs = make_rsrc(a.w, 0u);
-      s_rs = make_rsrc(a.scales, 0u);
-      b_rs = make_rsrc(a.biases, 0u);
+  auto w_next = [&]() {
+    w_kb += D;
+    if (w_kb == nit) {
+      w_kb = 0;
+      w_p += TN;
+      if constexpr (kBuf) {
+        w_rs = w_rsrc(w_p);
+        if constexpr (!SBB) {
+          ws_rs = s_rsrc(w_p);
+          wb_rs = b_rsrc(w_p);
+        }
+      }
     }
   };
 
-  // ---- activations first (their loads must retire before the weight prefetch), then the
-  // first block's loads, then the LDS writes of the first staging batch, then any others
-  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
-  const int nbatch = stage_batches<MROWS>(K, kThreads);
-  {
-    XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kThreads);
+  // ---- scale/bias stream (SBB): next sub-block to load is slots [s_kb, s_kb + D) of pair s_p
+  int64_t s_p = t_begin;
+  int s_kb = 0;
+  __amdgpu_buffer_rsrc_t s_rs, b_rs;
+  if constexpr (SBB) {
+    s_rs = s_rsrc(s_p);
+    b_rs = b_rsrc(s_p);
+  }
+  SbRegs<NHB> scA[TN], biA[TN], scB[TN], biB[TN];
+  auto issue_sb = [&](SbRegs<NHB>(&sc)[TN], SbRegs<NHB>(&bi)[TN]) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) issue_slot(j);
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kThreads);
-  }
-  for (int batch = 1; batch < nbatch; ++batch) {
+    for (int t = 0; t < TN; ++t) {
+      load_sb_buf<NHB>(sc[t], s_rs, sb_voff[t], s_kb * S::kGroups * 2);
+      load_sb_buf<NHB>(bi[t], b_rs, sb_voff[t], s_kb * S::kGroups * 2);
+    }
+    s_kb += D;
+    if (s_kb == nit) {
+      s_kb = 0;
+      s_p += TN;
+      s_rs = s_rsrc(s_p);
+      b_rs = b_rsrc(s_p);
+    }
+  };
+
+  // ---- prologue.  A wave that is queueing loads behind the chip-wide weight prefetch
+  // blocks every barrier it has not reached yet, so the activation staging and its barriers
+  // come first and the weight prefetch after them.
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
+  const int nbatch = stage_batches<MROWS>(K, kStreamThreads);
+  for (int batch = 0; batch < nbatch; ++batch) {
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kThreads);
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kThreads);
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
   }
+  zero_sx_pad<MT>(sxs, K / GS, tid);
   lds_barrier();
-  sum_x<T, GS, MT>(xs, sxs, K, wave, kWaves, lane);
+  sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
   lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SBB) issue_sb(scA, biA);
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue_w(j, j);
+  w_next();
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue_w(j, D + j);
+  w_next();
+  __builtin_amdgcn_sched_barrier(0);
   if (t_end <= t_begin) return;
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[MT], part[MT];
+  f32x4 acc[TN][MT], part[TN][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    acc[mt] = zero4;
-    part[mt] = zero4;
-  }
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
-    for (int kb = 0; kb < nit; kb += D) {
-      // consume the block slot by slot, refilling each slot with the next block's slot
-      advance();
+  for (int t = 0; t < TN; ++t)
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
-        consume_slot<T, BITS, GS, MT>(ring[j], xs, sxs, (kb + j) * S::kSpan, acc, part, lg, col, gshift);
-        issue_slot(j);
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[t][mt] = zero4;
+      part[t][mt] = zero4;
     }
-    store_tile<T, MT>(acc, yb, rows, tile * 16 + col, N, lg);
+
+  // ---- consumption: sub-block = D slots of ring half `rbase`, scale/bias set (sc, bi);
+  // the next sub-block's scales/biases go to the other set, each consumed slot is refilled
+  // right away with the slot 2*D ahead (the scheduling barriers keep the refills there)
+  int64_t c_p = t_begin;
+  int c_kb = 0;
+  auto sub_block = [&](int rbase, const SbRegs<NHB>(&sc)[TN], const SbRegs<NHB>(&bi)[TN],
+                       SbRegs<NHB>(&sc_next)[TN], SbRegs<NHB>(&bi_next)[TN]) {
+    if constexpr (SBB) issue_sb(sc_next, bi_next);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4;
+    for (int j = 0; j < D; ++j) {
+      if constexpr (SBB) {
+        consume_slot<T, BITS, GS, MT, TN, NHB>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
+                                               (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+      } else {
+        SbRegs<S::kGroups> s1[TN], b1[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          s1[t] = ring[rbase + j][t].s;
+          b1[t] = ring[rbase + j][t].b;
+        }
+        consume_slot<T, BITS, GS, MT, TN, S::kGroups>(ring[rbase + j], s1, b1, 0, xs, sxs, (c_kb + j) * S::kSpan,
+                                                      acc, part, lg, col, gshift);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(j, rbase + j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    w_next();
+    c_kb += D;
+    if (c_kb == nit) {
+      if (kYLds && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
+        store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          if (c_p + t < t_end) store_tile<T, MT>(acc[t], yb, rows, (c_p + t) * 16 + col, N, lg);
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = zero4;
+      c_kb = 0;
+      c_p += TN;
+    }
+  };
+  const int64_t nsub = (t_end - t_begin + TN - 1) / TN * (nit / D);
+  for (int64_t i = 0; i < nsub; i += 2) {
+    sub_block(0, scA, biA, scB, biB);
+    if (i + 1 < nsub) sub_block(D, scB, biB, scA, biA);
   }
 }
 
@@ -161,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   constexpr int MROWS = 16 * MT;
   constexpr int KC = kChunkXBytes / (MROWS * 2);
   __shared__ u32x4 xs[kChunkXBytes / 16];
-  __shared__ float sxs[(KC / 32) * MROWS];
+  __shared__ float sxs[(KC / 32 + kSxPad) * MROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -212,6 +322,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     const int kcl = min(KC, K - kc0);
     lds_barrier();
     stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads);
+    zero_sx_pad<MT>(sxs, kcl / GS, tid);
     lds_barrier();
     sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane);
     lds_barrier();
@@ -220,9 +331,16 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     for (int i = 0; i < nit; ++i) {
       const int kit = kit0 + i;
       issue(nxt, min(kit + 1, nit_total - 1));
+      {
+        SbRegs<S::kGroups> sc[TN], bi[TN];
 #pragma unroll
-      for (int t = 0; t < TN; ++t)
-        consume_slot<T, BITS, GS, MT>(cur[t], xs, sxs, i * S::kSpan, acc[t], part[t], lg, col, gshift);
+        for (int t = 0; t < TN; ++t) {
+          sc[t] = cur[t].s;
+          bi[t] = cur[t].b;
+        }
+        consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg, col,
+                                                      gshift);
+      }
 #pragma unroll
       for (int t = 0; t < TN; ++t) cur[t] = nxt[t];
     }
@@ -234,16 +352,16 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
 // ----------------------------------------------------------------------------- launchers
 int device_cus();
 
-template <class T, int BITS, int GS, int MT, int D>
-hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
-  auto kern = qmv_stream_kernel<T, BITS, GS, MT, D>;
+template <class T, int BITS, int GS, int MT, int D, bool SBB>
+hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
+  auto kern = qmv_stream_kernel<T, BITS, GS, MT, D, SBB>;
   static int per_cu = -1;  // occupancy for this instantiation (same LDS class each call)
   static int lds_cached = -1;
   if (lds_cached != lds) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kStreamThreads, lds);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
     lds_cached = lds;
@@ -254,12 +372,24 @@ hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
 #define QMM_MAX_WG_PER_CU 8
 #endif
   const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
-  const int64_t blocks = std::min<int64_t>(full, (n_tiles + kWaves - 1) / kWaves);
-  const int64_t waves_total = blocks * kWaves;
+  const int64_t blocks = std::min<int64_t>(full, (n_tiles + kStreamWaves - 1) / kStreamWaves);
+  const int64_t waves_total = blocks * kStreamWaves;
   if (n_tiles / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kThreads), lds, stream, a,
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a,
                      (int)(n_tiles / waves_total), (int)(n_tiles % waves_total));
   return hipGetLastError();
+}
+
+// Scales/biases per sub-block when their rows and bases are aligned to the load width.
+template <class T, int BITS, int GS, int MT, int D>
+hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
+  if constexpr (BITS == 4 || BITS == 8) {
+    constexpr int bytes = D * Slot<BITS, GS>::kGroups * 2;
+    constexpr int align = bytes < 16 ? bytes : 16;
+    if ((a.sb_row_stride * 2) % align == 0 && (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
+      return launch_stream_sb<T, BITS, GS, MT, D, true>(a, stream, lds);
+  }
+  return launch_stream_sb<T, BITS, GS, MT, D, false>(a, stream, lds);
 }
 
 // Slots per main-loop block: the largest of 8, 4, 2, 1 dividing the slots per tile.
@@ -267,7 +397,7 @@ template <class T, int BITS, int GS, int MT>
 hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
   const int nit = (int)(a.K / Slot<BITS, GS>::kSpan);
 #ifndef QMM_MAX_BLOCK_SLOTS
-#define QMM_MAX_BLOCK_SLOTS 4
+#define QMM_MAX_BLOCK_SLOTS 2
 #endif
   if (QMM_MAX_BLOCK_SLOTS >= 8 && nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
   if (QMM_MAX_BLOCK_SLOTS >= 4 && nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
@@ -285,7 +415,7 @@ hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
 
 template <int MT, int GS>
 constexpr int stream_lds_bytes(int K) {
-  return 16 * MT * K * 2 + (K / GS) * 16 * MT * 4;
+  return 16 * MT * K * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0);
 }
 
 template <class T, int BITS, int GS>
