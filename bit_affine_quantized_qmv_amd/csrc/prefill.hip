@@ -13,160 +13,218 @@
 namespace qmm {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int BM = 256;           // output rows per workgroup
+constexpr int BN = 256;           // output columns (weight rows) per workgroup
+constexpr int BK = 64;            // k per main-loop step
+constexpr int WM = 4, WN = 2;     // waves along M and N; each wave owns a (BM/WM) x (BN/WN) tile
+constexpr int kThreads = 64 * WM * WN;
+
+// BITS consecutive code words (32 codes) of one weight row, starting at a 32-code boundary.
+template <int BITS>
+__device__ inline void load_codes(uint32_t (&w)[BITS], const uint32_t* p) {
+  if constexpr (BITS % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) {
+      const u32x4 u = *(const u32x4*)(p + 4 * i);
+      w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+    }
+  } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i) {
+      const uint2 u = *(const uint2*)(p + 2 * i);
+      w[2 * i] = u.x; w[2 * i + 1] = u.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) w[i] = p[i];
+  }
+}
+
+// 32 codes -> w~ = RNE_dtype(fma(s, q, b)) as four 8-value MFMA operand chunks, k order.
+template <class T, int BITS>
+__device__ inline void dequant32(const uint32_t (&w)[BITS], float s, float b, u32x4 (&out)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float q[8];
+    if constexpr (BITS == 4) {
+      // nibbles to bytes, then the fp8 conversion: byte patterns 0..15 are c * 2^-9 in e4m3
+      const uint32_t even = w[c] & 0x0F0F0F0Fu, odd = (w[c] >> 4) & 0x0F0F0F0Fu;
+      const auto e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, 512.0f, false);
+      const auto e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(even, 512.0f, true);
+      const auto o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, 512.0f, false);
+      const auto o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(odd, 512.0f, true);
+      q[0] = e0[0]; q[2] = e0[1]; q[4] = e1[0]; q[6] = e1[1];
+      q[1] = o0[0]; q[3] = o0[1]; q[5] = o1[0]; q[7] = o1[1];
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[e] = (float)((w[2 * c] >> (8 * e)) & 0xFFu);
+        q[4 + e] = (float)((w[2 * c + 1] >> (8 * e)) & 0xFFu);
+      }
+    } else {
+      // codes 8c .. 8c+7 start at bit 8*c*BITS of the 32-code run
+      const int bit0 = 8 * c * BITS;
+      const uint32_t lo = w[bit0 >> 5];
+      const uint32_t hi = (bit0 >> 5) + 1 < BITS ? w[(bit0 >> 5) + 1] : 0u;
+      const uint64_t v = ((((uint64_t)hi) << 32) | lo) >> (bit0 & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = (float)((uint32_t)(v >> (e * BITS)) & ((1u << BITS) - 1u));
+    }
+    out[c].x = T::pack2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
+    out[c].y = T::pack2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
+    out[c].z = T::pack2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
+    out[c].w = T::pack2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
+  }
+}
 
 template <class T, int BITS>
-__global__ __launch_bounds__(kThreads) void qmm_prefill_kernel(const MatArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs a, const int m_tiles) {
   // operand layout in LDS: [buffer][k step (32)][lane group (8 k)][row] of 8 elements
   __shared__ u32x4 As[2][BK / 32][4][BM];
   __shared__ u32x4 Bs[2][BK / 32][4][BN];
+  constexpr int TM = BM / WM, TN = BN / WN;      // wave tile
+  constexpr int FM = TM / 16, FN = TN / 16;      // 16x16 MFMA blocks per wave tile
+  constexpr int A_PER = BM * (BK / 8) / kThreads;   // 16-byte activation chunks per thread
+  static_assert(BN * 2 == kThreads, "one thread per 32 codes of a weight row");
+  static_assert(A_PER <= FM && FM == 4, "activation and weight chunks are stored one per MFMA row");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lg = lane >> 4;
   const int col = lane & 15;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  // M-tile fastest: consecutive workgroups (which the dispatcher spreads over the XCDs)
+  // share a weight tile, and each XCD keeps seeing the same activation rows
+  const int mt = (int)(blockIdx.x % (unsigned)m_tiles);
+  const int nt = (int)(blockIdx.x / (unsigned)m_tiles);
   const int64_t z = blockIdx.z;
   const int64_t rows = a.rows_per_batch;
   const int64_t N = a.N;
   const int K = (int)a.K;
   const int gs = a.group_size;
-  const int64_t bm0 = (int64_t)blockIdx.y * BM;
-  const int64_t bn0 = (int64_t)blockIdx.x * BN;
+  const int64_t bm0 = (int64_t)mt * BM;
+  const int64_t bn0 = (int64_t)nt * BN;
   const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
 
-  // Global-load assignments: 4 chunks of 8 k per thread for A and for W.
-  const uint16_t* arow[4];
-  const uint32_t* wrow[4];
-  const uint16_t* srow[4];
-  const uint16_t* brow[4];
-  int jk[4];
+  // activation chunks: q -> row (q % 16) + 16 * (q / 128), chunk (q / 16) % 8, so a wave
+  // reads 64 contiguous bytes of 16 rows and writes four 256-byte runs of LDS
+  // rows past the call's rows read row 0 (always valid) and are zeroed after the load
+  const uint16_t* arow[A_PER];
+  int ar[A_PER], ac[A_PER];
+  uint32_t amask[A_PER];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + kThreads * i;
-    const int r = id >> 3;
-    jk[i] = id & 7;
-    const int64_t m = bm0 + r;
-    arow[i] = m < rows ? xb + (m / a.seg_rows) * a.seg_stride + (m % a.seg_rows) * a.row_stride
-                       : nullptr;
-    const int64_t n = bn0 + r;
-    const int64_t nl = n < N ? n : N - 1;
-    wrow[i] = a.w + nl * a.w_row_stride;
-    srow[i] = (const uint16_t*)a.scales + nl * a.sb_row_stride;
-    brow[i] = (const uint16_t*)a.biases + nl * a.sb_row_stride;
+  for (int i = 0; i < A_PER; ++i) {
+    const int q = tid + kThreads * i;
+    ar[i] = (q & 15) + 16 * (q >> 7);
+    ac[i] = (q >> 4) & 7;
+    const int64_t m = bm0 + ar[i];
+    const int64_t mr = m < rows ? m : 0;
+    amask[i] = m < rows ? 0xFFFFFFFFu : 0u;
+    arow[i] = xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride + 8 * ac[i];
   }
+  // weight: thread -> row wr, 32-code half wh of the 64 k of a step
+  const int wr = tid >> 1, wh = tid & 1;
+  const int64_t wn_row = bn0 + wr < N ? bn0 + wr : N - 1;
+  const uint32_t* wrow = a.w + wn_row * a.w_row_stride + wh * BITS;
+  const uint16_t* srow = (const uint16_t*)a.scales + wn_row * a.sb_row_stride;
+  const uint16_t* brow = (const uint16_t*)a.biases + wn_row * a.sb_row_stride;
 
-  u32x4 ra[4];
-  uint32_t rw0[4], rw1[4], rsb[4];
-  auto gload = [&](int k0) {
+  u32x4 ra[A_PER];
+  uint32_t rw[BITS];
+  uint32_t rs = 0, rb = 0;
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + 8 * jk[i];
-      ra[i] = arow[i] ? *(const u32x4*)(arow[i] + k) : u32x4{0u, 0u, 0u, 0u};
-      if (BITS == 4) {
-        rw0[i] = wrow[i][k >> 3];
-        rw1[i] = 0u;
-      } else if (BITS == 8) {
-        rw0[i] = wrow[i][k >> 2];
-        rw1[i] = wrow[i][(k >> 2) + 1];
-      } else {
-        const int row_words = (K * BITS) >> 5;
-        const int bit0 = k * BITS;
-        const int idx = bit0 >> 5;
-        rw0[i] = wrow[i][idx];
-        rw1[i] = wrow[i][min(idx + 1, row_words - 1)];
-      }
-      const int gi = k / gs;
-      rsb[i] = (uint32_t)srow[i][gi] | ((uint32_t)brow[i][gi] << 16);
-    }
+    for (int i = 0; i < A_PER; ++i) ra[i] = *(const u32x4*)(arow[i] + k0) & amask[i];
+    load_codes<BITS>(rw, wrow + kt * (BK * BITS / 32));
+    const int g = (k0 + 32 * wh) / gs;
+    rs = srow[g];
+    rb = brow[g];
   };
-  auto lstore = [&](int buf, int k0) {
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid + kThreads * i) >> 3;
-      const int ks = jk[i] >> 2;
-      const int g = jk[i] & 3;
-      As[buf][ks][g][r] = ra[i];
-      const float s = T::to_f32(rsb[i] & 0xFFFFu);
-      const float b = T::to_f32(rsb[i] >> 16);
-      float q[8];
-      if (BITS == 4) {
+    for (int i = 0; i < A_PER; ++i) As[buf][ac[i] >> 2][ac[i] & 3][ar[i]] = ra[i];
+    u32x4 wv[4];
+    dequant32<T, BITS>(rw, T::to_f32(rs), T::to_f32(rb), wv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = (float)((rw0[i] >> (4 * e)) & 0xFu);
-      } else if (BITS == 8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          q[e] = (float)((rw0[i] >> (8 * e)) & 0xFFu);
-          q[4 + e] = (float)((rw1[i] >> (8 * e)) & 0xFFu);
-        }
-      } else {
-        const int k = k0 + 8 * jk[i];
-        const uint64_t v = ((((uint64_t)rw1[i]) << 32) | rw0[i]) >> ((k * BITS) & 31);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = (float)((uint32_t)(v >> (e * BITS)) & ((1u << BITS) - 1u));
-      }
-      u32x4 wv;
-      wv.x = T::pack2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
-      wv.y = T::pack2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
-      wv.z = T::pack2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
-      wv.w = T::pack2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
-      Bs[buf][ks][g][r] = wv;
-    }
+    for (int c = 0; c < 4; ++c) Bs[buf][wh][c][wr] = wv[c];
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[FM][FN];
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero4;
 
-  const int nk = K / BK;
+  // Software pipeline over k steps: while the MFMAs of step kt read LDS buffer kt & 1, the
+  // registers holding step kt+1's global data are dequantized and written to the other
+  // buffer, interleaved with the first half of the MFMAs; the loads of step kt+2 are then
+  // issued into the freed registers.  One barrier per step.  The body has no branches: the
+  // last step reloads a clamped step and writes it into the buffer no one reads any more.
+  const int nk = K / BK;   // >= 2 (K is a multiple of 128)
   gload(0);
-  lstore(0, 0);
+  lstore(0);
+  gload(1);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    typename T::v8 av[FM], bv[FN];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      typename T::v8 av[4], bv[4];
+    for (int i = 0; i < FM; ++i) av[i] = as_v8<T>(As[buf][0][lg][wm * TM + 16 * i + col]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = as_v8<T>(As[buf][ks][lg][wm * 64 + 16 * i + col]);
+    for (int j = 0; j < FN; ++j) bv[j] = as_v8<T>(Bs[buf][0][lg][wn * TN + 16 * j + col]);
+    u32x4 wv[4];
+    dequant32<T, BITS>(rw, T::to_f32(rs), T::to_f32(rb), wv);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = as_v8<T>(Bs[buf][ks][lg][wn * 64 + 16 * j + col]);
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
+      // one activation chunk and one weight chunk per MFMA row
+      if (i < A_PER) As[buf ^ 1][ac[i] >> 2][ac[i] & 3][ar[i]] = ra[i];
+      Bs[buf ^ 1][wh][i][wr] = wv[i];
     }
-    if (kt + 1 < nk) lstore(buf ^ 1, (kt + 1) * BK);
+    // spread the dequantization and the LDS writes between the MFMAs of the first half
+#pragma unroll
+    for (int t = 0; t < FM * FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+      if (t % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+    }
+    gload(kt + 2 < nk ? kt + 2 : nk - 1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) av[i] = as_v8<T>(As[buf][1][lg][wm * TM + 16 * i + col]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[j] = as_v8<T>(Bs[buf][1][lg][wn * TN + 16 * j + col]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
     __syncthreads();
   }
 
   uint16_t* yb = (uint16_t*)a.y + z * rows * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = bm0 + wm * 64 + 16 * i + 4 * lg + r;
-        const int64_t n = bn0 + wn * 64 + 16 * j + col;
+        const int64_t m = bm0 + wm * TM + 16 * i + 4 * lg + r;
+        const int64_t n = bn0 + wn * TN + 16 * j + col;
         if (m < rows && n < N) yb[m * N + n] = T::from_f32(acc[i][j][r]);
       }
 }
 
 template <class T, int BITS>
 hipError_t launch_bits(const MatArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.rows_per_batch + BM - 1) / BM),
-            (unsigned)a.batches);
-  hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a);
+  const int64_t m_tiles = (a.rows_per_batch + BM - 1) / BM;
+  const int64_t n_tiles = (a.N + BN - 1) / BN;
+  if (m_tiles * n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), dim3((unsigned)(m_tiles * n_tiles), 1, (unsigned)a.batches),
+                     dim3(kThreads), 0, stream, a, (int)m_tiles);
   return hipGetLastError();
 }
 
@@ -186,8 +244,7 @@ hipError_t launch_dtype(const MatArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const MatArgs& a, hipStream_t stream) {
-  if (a.rows_per_batch <= 0 || a.batches > 65535 || (a.rows_per_batch + BM - 1) / BM > 65535)
-    return hipErrorInvalidValue;
+  if (a.rows_per_batch <= 0 || a.batches > 65535 || a.K % BK != 0) return hipErrorInvalidValue;
   return a.dtype == 1 ? launch_dtype<Bf16>(a, stream) : launch_dtype<Fp16>(a, stream);
 }
 
