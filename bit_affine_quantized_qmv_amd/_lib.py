@@ -23,7 +23,7 @@ ERRORS = {
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
 # Every symbol include/qmm.h declares.
-EXPORTS = ("qmm_abi_version", "qmm_last_error", "qmm_quantize", "qmv", "qmm_t", "qmm_plan")
+EXPORTS = ("qmm_abi_version", "qmm_last_error", "qmm_quantize", "qmv", "qmm_t", "qmm_plan", "qmm_gather_qmv")
 
 
 class TensorDesc(ctypes.Structure):
@@ -89,6 +89,9 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int32
         fn.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), P,
                        ctypes.POINTER(TensorDesc), ctypes.c_uint32, P]
+    lib.qmm_gather_qmv.restype = ctypes.c_int32
+    lib.qmm_gather_qmv.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, P, P, ctypes.POINTER(TensorDesc), P]
     lib.qmm_plan.restype = ctypes.c_int32
     lib.qmm_plan.argtypes = [ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc),
                              ctypes.POINTER(TensorDesc), ctypes.c_uint32, ctypes.c_int32,

@@ -89,6 +89,51 @@ def qmm_t(x: torch.Tensor, qw: QuantizedWeight, flags: int = 0, out=None) -> tor
     return _matmul(1, x, qw, flags, out)
 
 
+@dataclass
+class ExpertWeights:
+    """A stack of E quantized weights: w_packed [E, N, words], scales/biases [E, N, K/gs]."""
+    w_packed: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+    N: int
+    K: int
+    group_size: int
+    bits: int
+
+    @staticmethod
+    def stack(weights) -> "ExpertWeights":
+        q0 = weights[0]
+        return ExpertWeights(torch.stack([q.w_packed for q in weights]), torch.stack([q.scales for q in weights]),
+                             torch.stack([q.biases for q in weights]), q0.N, q0.K, q0.group_size, q0.bits)
+
+    @property
+    def num_experts(self) -> int:
+        return self.w_packed.shape[0]
+
+    def expert(self, e: int) -> QuantizedWeight:
+        return QuantizedWeight(self.w_packed[e], self.scales[e], self.biases[e], self.N, self.K, self.group_size,
+                               self.bits)
+
+
+def gather_qmv(x: torch.Tensor, experts: ExpertWeights, expert_index: torch.Tensor, out=None) -> torch.Tensor:
+    """Row r of x times expert expert_index[r]'s dequantized weight (qmm_gather_qmv)."""
+    lib = _lib.load()
+    assert expert_index.dtype == torch.int32 and expert_index.is_cuda and expert_index.is_contiguous()
+    rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
+    if expert_index.numel() != rows:
+        raise ValueError("gather_qmv: %d expert indices for %d activation rows" % (expert_index.numel(), rows))
+    y = out if out is not None else torch.empty(*x.shape[:-1], experts.N, dtype=x.dtype, device=x.device)
+    if x.dtype != experts.scales.dtype or y.dtype != x.dtype:
+        raise _lib.QmmError(-2, "x, y, scales and biases must share one dtype")
+    wd = experts.expert(0).desc()
+    xd = _lib.tensor_desc(x.shape, x.stride())
+    yd = _lib.tensor_desc(y.shape, y.stride())
+    _lib.check(lib.qmm_gather_qmv(x.data_ptr(), ctypes.byref(xd), ctypes.byref(wd), experts.num_experts,
+                                  experts.w_packed.stride(0), experts.scales.stride(0), expert_index.data_ptr(),
+                                  y.data_ptr(), ctypes.byref(yd), _stream(x.device)))
+    return y
+
+
 def plan(x_shape, x_stride, N: int, K: int, group_size: int = 64, bits: int = 4,
          dtype: int = _lib.QMM_BF16, entry: int = 1, flags: int = 0, y_shape=None, y_stride=None) -> dict:
     """Host-only dispatcher query (qmm_plan): the plan, or QmmError."""

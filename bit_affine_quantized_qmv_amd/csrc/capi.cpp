@@ -22,14 +22,8 @@ int32_t launch_status(hipError_t e) {
   return finish(QMM_ERR_HIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
 }
 
-int32_t run_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_desc_t* w, void* y,
-                   const qmm_tensor_desc_t* yd, uint32_t flags, void* stream, int entry) {
-  std::string err;
-  qmm_plan_t p;
-  const int rc = qmm::plan_matmul(x, xd, w, y, yd, flags, entry, true, &p, &err);
-  if (rc != QMM_OK) return finish(rc, err);
-  if (p.rows == 0 || w->N == 0) return finish(QMM_OK, "");
-  qmm::MatArgs a;
+qmm::MatArgs make_args(const void* x, const qmm_plan_t& p, const qmm_weight_desc_t* w, void* y) {
+  qmm::MatArgs a{};
   a.x = x;
   a.batches = p.batches;
   a.batch_stride = p.batch_stride;
@@ -48,6 +42,17 @@ int32_t run_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_
   a.group_size = w->group_size;
   a.bits = w->bits;
   a.dtype = w->dtype;
+  return a;
+}
+
+int32_t run_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_desc_t* w, void* y,
+                   const qmm_tensor_desc_t* yd, uint32_t flags, void* stream, int entry) {
+  std::string err;
+  qmm_plan_t p;
+  const int rc = qmm::plan_matmul(x, xd, w, y, yd, flags, entry, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0 || w->N == 0) return finish(QMM_OK, "");
+  const qmm::MatArgs a = make_args(x, p, w, y);
   hipStream_t s = (hipStream_t)stream;
   return launch_status(p.family == 0 ? qmm::launch_decode(a, s) : qmm::launch_prefill(a, s));
 }
@@ -59,6 +64,31 @@ extern "C" {
 int32_t qmm_abi_version(void) { return QMM_ABI_VERSION; }
 
 const char* qmm_last_error(void) { return g_error.c_str(); }
+
+int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+                       int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
+                       const int32_t* expert_index, void* y, const qmm_tensor_desc_t* y_desc, void* stream) {
+  std::string err;
+  qmm_plan_t p;
+  // one grid slice per activation row: the forced per-row plan of the row layout
+  int rc = qmm::plan_matmul(x, x_desc, w, y, y_desc, QMM_FLAG_FORCE_STRIDED, 1, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0 || w->N == 0) return finish(QMM_OK, "");
+  if (p.rows_per_batch != 1)
+    return finish(QMM_ERR_LAYOUT, "gather_qmv: x rows must fold into one strided level");
+  if (num_experts < 1) return finish(QMM_ERR_SHAPE, "gather_qmv: num_experts must be >= 1");
+  if (!expert_index) return finish(QMM_ERR_NULL, "gather_qmv: expert_index must be non-NULL");
+  if ((uintptr_t)expert_index % 4) return finish(QMM_ERR_ALIGN, "gather_qmv: expert_index must be 4-byte aligned");
+  if (w_expert_stride < w->N * w->w_row_stride || sb_expert_stride < w->N * w->sb_row_stride)
+    return finish(QMM_ERR_SHAPE, "gather_qmv: expert strides smaller than one expert's weight");
+  if (w_expert_stride % 4) return finish(QMM_ERR_ALIGN, "gather_qmv: w_expert_stride must be a multiple of 4 words");
+  qmm::MatArgs a = make_args(x, p, w, y);
+  a.w_index = expert_index;
+  a.num_experts = num_experts;
+  a.w_expert_stride = w_expert_stride;
+  a.sb_expert_stride = sb_expert_stride;
+  return launch_status(qmm::launch_decode(a, (hipStream_t)stream));
+}
 
 int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride, int32_t group_size,
                      int32_t bits, int32_t dtype, uint32_t* w_packed, void* scales, void* biases,

@@ -398,6 +398,35 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
   }
 }
 
+// Weight, scale and bias bases of grid batch z: the call's own, or those of the expert the
+// batch's index selects (index out of range -> expert 0 is read, and *bad is set so the
+// caller stores NaN).
+struct WeightBase {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  bool bad;
+};
+
+__device__ inline WeightBase weight_base(const MatArgs& a, int64_t z) {
+  WeightBase r{a.w, (const uint16_t*)a.scales, (const uint16_t*)a.biases, false};
+  if (a.w_index) {
+    const int e = __builtin_amdgcn_readfirstlane(a.w_index[z]);
+    r.bad = e < 0 || e >= a.num_experts;
+    const int64_t ec = r.bad ? 0 : e;
+    r.w += ec * a.w_expert_stride;
+    r.s += ec * a.sb_expert_stride;
+    r.b += ec * a.sb_expert_stride;
+  }
+  return r;
+}
+
+template <int MT>
+__device__ inline void poison(f32x4 (&acc)[MT]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+}
+
 template <class T, int MT>
 __device__ inline void store_tile(const f32x4 (&acc)[MT], uint16_t* yb, int rows, int64_t n, int64_t N,
                                   int lg) {

@@ -102,13 +102,10 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     valid = valid < (t_end - p) * 16 ? valid : (t_end - p) * 16;
     return (uint32_t)valid;
   };
-  auto w_rsrc = [&](int64_t p) { return make_rsrc(a.w + p * 16 * a.w_row_stride, rows_valid(p) * w_row_bytes); };
-  auto s_rsrc = [&](int64_t p) {
-    return make_rsrc((const uint16_t*)a.scales + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes);
-  };
-  auto b_rsrc = [&](int64_t p) {
-    return make_rsrc((const uint16_t*)a.biases + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes);
-  };
+  const WeightBase wb = weight_base(a, z);
+  auto w_rsrc = [&](int64_t p) { return make_rsrc(wb.w + p * 16 * a.w_row_stride, rows_valid(p) * w_row_bytes); };
+  auto s_rsrc = [&](int64_t p) { return make_rsrc(wb.s + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes); };
+  auto b_rsrc = [&](int64_t p) { return make_rsrc(wb.b + p * 16 * a.sb_row_stride, rows_valid(p) * sb_row_bytes); };
 
   // ---- weight stream: next sub-block to load is slots [w_kb, w_kb + D) of pair w_p
   int64_t w_p = t_begin;
@@ -132,9 +129,9 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
       } else {
         const int64_t n = w_p * 16 + 16 * t + col;
         const int64_t nl = n < N ? n : N - 1;
-        load_slot<BITS, GS>(ring[r][t], a.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
-                            (const uint16_t*)a.scales + nl * a.sb_row_stride + kit * S::kGroups,
-                            (const uint16_t*)a.biases + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
+        load_slot<BITS, GS>(ring[r][t], wb.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
+                            wb.s + nl * a.sb_row_stride + kit * S::kGroups,
+                            wb.b + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
                             row_words - kit * S::kRowWordsPerSlot);
       }
     }
@@ -243,6 +240,10 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     w_next();
     c_kb += D;
     if (c_kb == nit) {
+      if (wb.bad) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) poison<MT>(acc[t]);
+      }
       if (kYLds && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
         store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
       } else {
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   uint32_t gshift = 0;
   if constexpr (BITS != 4 && BITS != 8) generic_lane_offsets<BITS>(lg, gword, gshift);
 
+  const WeightBase wb = weight_base(a, z);
   int64_t nrow[TN], nl[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
@@ -299,9 +301,9 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   auto issue = [&](SlotData<BITS, GS> (&d)[TN], int kit) {
 #pragma unroll
     for (int t = 0; t < TN; ++t)
-      load_slot<BITS, GS>(d[t], a.w + nl[t] * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
-                          (const uint16_t*)a.scales + nl[t] * a.sb_row_stride + kit * S::kGroups,
-                          (const uint16_t*)a.biases + nl[t] * a.sb_row_stride + kit * S::kGroups, lg, gword,
+      load_slot<BITS, GS>(d[t], wb.w + nl[t] * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
+                          wb.s + nl[t] * a.sb_row_stride + kit * S::kGroups,
+                          wb.b + nl[t] * a.sb_row_stride + kit * S::kGroups, lg, gword,
                           row_words - kit * S::kRowWordsPerSlot);
   };
 
@@ -345,6 +347,10 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
       for (int t = 0; t < TN; ++t) cur[t] = nxt[t];
     }
   }
+  if (wb.bad) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) poison<MT>(acc[t]);
+  }
 #pragma unroll
   for (int t = 0; t < TN; ++t) store_tile<T, MT>(acc[t], yb, rows, nrow[t], N, lg);
 }
@@ -386,7 +392,8 @@ hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
   if constexpr (BITS == 4 || BITS == 8) {
     constexpr int bytes = D * Slot<BITS, GS>::kGroups * 2;
     constexpr int align = bytes < 16 ? bytes : 16;
-    if ((a.sb_row_stride * 2) % align == 0 && (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
+    if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
+        (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
       return launch_stream_sb<T, BITS, GS, MT, D, true>(a, stream, lds);
   }
   return launch_stream_sb<T, BITS, GS, MT, D, false>(a, stream, lds);

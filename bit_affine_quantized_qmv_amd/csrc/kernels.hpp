@@ -28,6 +28,14 @@ struct MatArgs {
   int32_t group_size;
   int32_t bits;
   int32_t dtype;  // 1 = bf16, 2 = fp16
+  // Gathered weights (decode family only): when w_index is set, grid batch z (one activation
+  // row) uses expert e = w_index[z] of a stack of num_experts weights, i.e. w, scales and
+  // biases advanced by e * w_expert_stride words / e * sb_expert_stride elements.  An index
+  // outside [0, num_experts) makes the row's outputs NaN.
+  const int32_t* w_index = nullptr;
+  int64_t num_experts = 0;
+  int64_t w_expert_stride = 0;
+  int64_t sb_expert_stride = 0;
 };
 
 struct QuantArgs {

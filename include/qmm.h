@@ -142,6 +142,25 @@ int32_t qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_des
 int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
               void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
 
+/* Gathered-weight decode form (mixture-of-experts decode): a stack of num_experts
+ * quantized weights that share N, K, group_size, bits and dtype, expert e's codes at
+ * w->w_packed + e*w_expert_stride words and its scales/biases at w->scales / w->biases +
+ * e*sb_expert_stride elements; activation row r uses expert e = expert_index[r]:
+ *   y[r, :] = x[r, :] . dequant(W_e)^T.
+ * (MLX pull request 4516, pull request text: "Gathered QMV" is the expert-indexed variant of
+ * the affine qmv; "Correctness": covered with batched weights.  The Bits=8 final report,
+ * section 4.3, shows such expert stacks.)
+ * x: rows folding to ONE strided level (e.g. [M, K] or [M, 1, K]); y dense [..., N].
+ * expert_index: DEVICE array of x's row count int32 values.  Indices are read on the GPU; a
+ * row whose index is outside [0, num_experts) gets NaN outputs (nothing is read outside the
+ * stack).  Each row runs the decode kernels on its own (at most 65535 rows), and its result
+ * is bit-identical to qmv on that row with expert e's weight.
+ * Strides: w_expert_stride >= N * w_row_stride (a multiple of 4), sb_expert_stride >=
+ * N * sb_row_stride.  Other requirements as for qmv.  Zero rows or N == 0 is a no-op. */
+int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
+                       int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
+                       const int32_t* expert_index, void* y, const qmm_tensor_desc_t* y_desc, void* stream);
+
 /* Host-only: validate a qmv (entry = 0) or qmm_t (entry = 1) call and report its plan
  * without touching the GPU.  Pointers inside `w` are only checked for NULL/alignment when
  * they are non-NULL (pass NULLs to test layouts alone).  Returns QMM_OK or the same error

@@ -289,3 +289,28 @@ def reference(x_rows, w_packed, scales_bits, biases_bits, k_cols: int, group_siz
     w_deq = dequant(codes, scales_bits, biases_bits, group_size, dtype)
     y_ref = matmul_rows(x_rows, w_deq)
     return {"y_ref": y_ref, "tol": bound(x_rows, w_deq, y_ref, dtype), "w_deq": w_deq}
+
+
+# ----------------------------------------------------------------------------------
+# gathered weights (expert-indexed rows)
+# ----------------------------------------------------------------------------------
+def gather_reference(x_rows, experts, index, k_cols: int, group_size: int, bits: int,
+                     dtype: str) -> dict:
+    """Expert-indexed decode ([mlx-4516], pull request text: "Gathered QMV"; Correctness:
+    batched weights): output row r is x_rows[r] times the dequantized weight of expert
+    index[r].  `experts` is a list of (w_packed, scales_bits, biases_bits), one per expert.
+    Rows whose index lies outside [0, len(experts)) have y_ref = NaN and tol = 0 (the
+    library's documented answer for such rows).  Each row goes through `reference` alone."""
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    index = np.asarray(index)
+    n_out = int(np.asarray(experts[0][1]).shape[0])
+    y_ref = np.full((x_rows.shape[0], n_out), np.nan)
+    tol = np.zeros((x_rows.shape[0], n_out))
+    for r in range(x_rows.shape[0]):
+        e = int(index[r])
+        if 0 <= e < len(experts):
+            w_packed, sbits, bbits = experts[e]
+            one = reference(x_rows[r:r + 1], w_packed, sbits, bbits, k_cols, group_size, bits, dtype)
+            y_ref[r] = one["y_ref"][0]
+            tol[r] = one["tol"][0]
+    return {"y_ref": y_ref, "tol": tol}

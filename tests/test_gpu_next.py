@@ -1,0 +1,82 @@
+"""GPU parity tests of the rows that extend the hot path: gathered-weight decode, ..."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from qmm_testlib import TORCH_DTYPE, assert_close, half_bits, require_gpu, upload_oracle_weight, values, words
+
+pytestmark = pytest.mark.gpu
+
+
+def _experts(n, k, gs, bits, dtype, count, seed, dev):
+    import bit_affine_quantized_qmv_amd as q
+    ws = []
+    for e in range(count):
+        w = synth.normal_weight(n, k, 0.02, seed=seed + e).numpy()
+        ws.append(upload_oracle_weight(O.quantize(w, gs, bits, dtype), dev))
+    return q.ExpertWeights.stack(ws), ws
+
+
+def _oracle_triples(ws):
+    return [(words(q.w_packed), half_bits(q.scales), half_bits(q.biases)) for q in ws]
+
+
+@pytest.mark.parametrize("bits,gs,dtype", [(4, 64, "bf16"), (8, 64, "fp16"), (3, 32, "bf16"), (4, 128, "fp16")])
+def test_gather_qmv_parity(bits, gs, dtype):
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, k, e = 1000, 1024, 5
+    ex, ws = _experts(n, k, gs, bits, dtype, e, 700, dev)
+    idx = torch.tensor([3, 0, 4, 4, 1, 3, 2], dtype=torch.int32, device=dev)
+    x = synth.normal_x((7, k), dtype, seed=71).to(dev)
+    y = q.gather_qmv(x, ex, idx)
+    torch.cuda.synchronize()
+    ref = O.gather_reference(values(x), _oracle_triples(ws), idx.cpu().numpy(), k, gs, bits, dtype)
+    assert_close(y, ref, "gather_qmv")
+    # each row is the plain decode call on that row with its expert, bit for bit
+    for r in range(7):
+        y1 = q.qmv(x[r:r + 1], ws[int(idx[r])])
+        assert torch.equal(y1[0].view(torch.int16), y[r].view(torch.int16)), r
+
+
+def test_gather_qmv_bad_index_rows_nan_and_padded_stride():
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, k, gs, bits, dtype = 333, 512, 64, 4, "bf16"
+    ex, ws = _experts(n, k, gs, bits, dtype, 3, 720, dev)
+    # expert stack with padded per-expert strides (extra rows of NaN-poisoned scales)
+    words_pad = torch.zeros(3, n + 8, ex.w_packed.shape[2], dtype=torch.int32, device=dev)
+    sc_pad = torch.full((3, n + 8, ex.scales.shape[2]), float("nan"), dtype=TORCH_DTYPE[dtype], device=dev)
+    bi_pad = sc_pad.clone()
+    words_pad[:, :n] = ex.w_packed
+    sc_pad[:, :n] = ex.scales
+    bi_pad[:, :n] = ex.biases
+    exp = q.ExpertWeights(words_pad[:, :n], sc_pad[:, :n], bi_pad[:, :n], n, k, gs, bits)
+    idx = torch.tensor([2, -1, 0, 3, 1], dtype=torch.int32, device=dev)
+    x = synth.normal_x((5, k), dtype, seed=72).to(dev)
+    y = q.gather_qmv(x, exp, idx)
+    torch.cuda.synchronize()
+    yv = values(y)
+    assert np.isnan(yv[1]).all() and np.isnan(yv[3]).all()
+    ref = O.gather_reference(values(x), _oracle_triples(ws), idx.cpu().numpy(), k, gs, bits, dtype)
+    good = [0, 2, 4]
+    res = O.check(yv[good], ref["y_ref"][good], ref["tol"][good])
+    assert res["ok"], res
+
+
+def test_gather_qmv_errors():
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    ex, _ = _experts(64, 256, 64, 4, "bf16", 2, 730, dev)
+    x = synth.normal_x((3, 256), "bf16", seed=73).to(dev)
+    idx = torch.zeros(3, dtype=torch.int32, device=dev)
+    buf = synth.normal_x((2, 6, 256), "bf16", seed=74).to(dev)
+    with pytest.raises(q.QmmError) as e:   # rows that do not fold into one level
+        q.gather_qmv(buf[:, :3], ex, torch.zeros(6, dtype=torch.int32, device=dev))
+    assert e.value.code == -4
+    with pytest.raises(ValueError):        # one index per row
+        q.gather_qmv(buf[0], ex, idx)
+    y = torch.zeros(0, 64, dtype=torch.bfloat16, device=dev)
+    q.gather_qmv(x[:0], ex, idx[:0], out=y)    # zero rows: no-op
