@@ -23,7 +23,8 @@ ERRORS = {
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
 # Every symbol include/qmm.h declares.
-EXPORTS = ("qmm_abi_version", "qmm_last_error", "qmm_quantize", "qmv", "qmm_t", "qmm_plan", "qmm_gather_qmv")
+EXPORTS = ("qmm_abi_version", "qmm_last_error", "qmm_quantize", "qmv", "qmm_t", "qmm_plan", "qmm_gather_qmv",
+           "qmm_dequantize", "qmm_embedding")
 
 
 class TensorDesc(ctypes.Structure):
@@ -92,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.qmm_gather_qmv.restype = ctypes.c_int32
     lib.qmm_gather_qmv.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, P, P, ctypes.POINTER(TensorDesc), P]
+    lib.qmm_dequantize.restype = ctypes.c_int32
+    lib.qmm_dequantize.argtypes = [ctypes.POINTER(WeightDesc), P, ctypes.c_int64, P]
+    lib.qmm_embedding.restype = ctypes.c_int32
+    lib.qmm_embedding.argtypes = [ctypes.POINTER(WeightDesc), P, ctypes.c_int64, P, ctypes.c_int64, P]
     lib.qmm_plan.restype = ctypes.c_int32
     lib.qmm_plan.argtypes = [ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc),
                              ctypes.POINTER(TensorDesc), ctypes.c_uint32, ctypes.c_int32,

@@ -134,6 +134,28 @@ def gather_qmv(x: torch.Tensor, experts: ExpertWeights, expert_index: torch.Tens
     return y
 
 
+def dequantize(qw: QuantizedWeight, out=None) -> torch.Tensor:
+    """Dense [N, K] dtype matrix of the quantized weight (qmm_dequantize)."""
+    lib = _lib.load()
+    y = out if out is not None else torch.empty(qw.N, qw.K, dtype=qw.dtype, device=qw.w_packed.device)
+    assert y.dtype == qw.dtype and y.stride(1) == 1 and tuple(y.shape) == (qw.N, qw.K)
+    _lib.check(lib.qmm_dequantize(ctypes.byref(qw.desc()), y.data_ptr(), y.stride(0), _stream(y.device)))
+    return y
+
+
+def embedding(qw: QuantizedWeight, indices: torch.Tensor, out=None) -> torch.Tensor:
+    """Dequantized rows indices[r] of a quantized table (qmm_embedding); NaN rows for indices
+    outside [0, N)."""
+    lib = _lib.load()
+    assert indices.dtype == torch.int32 and indices.is_cuda and indices.is_contiguous()
+    count = indices.numel()
+    y = out if out is not None else torch.empty(count, qw.K, dtype=qw.dtype, device=indices.device)
+    assert y.dtype == qw.dtype and y.stride(1) == 1 and tuple(y.shape) == (count, qw.K)
+    _lib.check(lib.qmm_embedding(ctypes.byref(qw.desc()), indices.data_ptr(), count, y.data_ptr(), y.stride(0),
+                                 _stream(y.device)))
+    return y
+
+
 def plan(x_shape, x_stride, N: int, K: int, group_size: int = 64, bits: int = 4,
          dtype: int = _lib.QMM_BF16, entry: int = 1, flags: int = 0, y_shape=None, y_stride=None) -> dict:
     """Host-only dispatcher query (qmm_plan): the plan, or QmmError."""

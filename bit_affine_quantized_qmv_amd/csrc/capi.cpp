@@ -90,6 +90,58 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
   return launch_status(qmm::launch_decode(a, (hipStream_t)stream));
 }
 
+// Shared validation of the whole-row dequantization entry points.
+static int32_t run_dequant(const qmm_weight_desc_t* w, const int32_t* index, int64_t rows, void* out,
+                           int64_t out_row_stride, void* stream) {
+  if (!w) return finish(QMM_ERR_NULL, "w must be non-NULL");
+  std::string err;
+  int rc = qmm::check_codec(w->group_size, w->bits, w->dtype, &err);
+  if (rc) return finish(rc, err);
+  if (w->K <= 0 || w->N < 0 || rows < 0) return finish(QMM_ERR_SHAPE, "need K > 0, N >= 0 and rows >= 0");
+  if (w->K % w->group_size) return finish(QMM_ERR_SHAPE, "K is not a multiple of group_size");
+  if (w->w_row_stride < w->K * w->bits / 32 || w->sb_row_stride < w->K / w->group_size)
+    return finish(QMM_ERR_SHAPE, "w_row_stride or sb_row_stride smaller than a row");
+  if (out_row_stride < w->K) return finish(QMM_ERR_SHAPE, "out_row_stride < K");
+  if (rows == 0 || (!index && w->N == 0)) return finish(QMM_OK, "");
+  if (!w->w_packed || !w->scales || !w->biases || !out)
+    return finish(QMM_ERR_NULL, "w_packed, scales, biases and out must be non-NULL");
+  // a 32-code run is loaded with one access of its own size: 4 words for 4/8-bit codes,
+  // 2 words for 2/6-bit codes, single words otherwise
+  const int run_align = w->bits % 4 == 0 ? 4 : (w->bits % 2 == 0 ? 2 : 1);
+  if ((uintptr_t)w->w_packed % (4 * run_align) || w->w_row_stride % run_align)
+    return finish(QMM_ERR_ALIGN, "w_packed / w_row_stride not aligned to the code runs");
+  if ((uintptr_t)w->scales % 2 || (uintptr_t)w->biases % 2) return finish(QMM_ERR_ALIGN, "scales/biases alignment");
+  if ((uintptr_t)out % 16 || out_row_stride % 8)
+    return finish(QMM_ERR_ALIGN, "out must be 16-byte aligned with a row stride that is a multiple of 8");
+  if (index && (uintptr_t)index % 4) return finish(QMM_ERR_ALIGN, "indices must be 4-byte aligned");
+  qmm::DequantArgs a{};
+  a.w = w->w_packed;
+  a.w_row_stride = w->w_row_stride;
+  a.scales = w->scales;
+  a.biases = w->biases;
+  a.sb_row_stride = w->sb_row_stride;
+  a.N = w->N;
+  a.K = w->K;
+  a.group_size = w->group_size;
+  a.bits = w->bits;
+  a.dtype = w->dtype;
+  a.index = index;
+  a.rows = rows;
+  a.out = out;
+  a.out_row_stride = out_row_stride;
+  return launch_status(qmm::launch_dequant(a, (hipStream_t)stream));
+}
+
+int32_t qmm_dequantize(const qmm_weight_desc_t* w, void* out, int64_t out_row_stride, void* stream) {
+  return run_dequant(w, nullptr, w ? w->N : 0, out, out_row_stride, stream);
+}
+
+int32_t qmm_embedding(const qmm_weight_desc_t* w, const int32_t* indices, int64_t count, void* out,
+                      int64_t out_row_stride, void* stream) {
+  if (count > 0 && !indices) return finish(QMM_ERR_NULL, "indices must be non-NULL");
+  return run_dequant(w, indices, count, out, out_row_stride, stream);
+}
+
 int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride, int32_t group_size,
                      int32_t bits, int32_t dtype, uint32_t* w_packed, void* scales, void* biases,
                      void* stream) {

@@ -51,10 +51,31 @@ struct QuantArgs {
   void* biases;
 };
 
+// Dequantization of whole weight rows: out row r = dequant(W[src(r)]), src(r) = index[r] when
+// index is set (an embedding-row gather; out-of-range -> NaN row), else r.
+struct DequantArgs {
+  const uint32_t* w;
+  int64_t w_row_stride;
+  const void* scales;
+  const void* biases;
+  int64_t sb_row_stride;
+  int64_t N;          // weight rows
+  int64_t K;
+  int32_t group_size;
+  int32_t bits;
+  int32_t dtype;
+  const int32_t* index;
+  int64_t rows;       // output rows
+  void* out;
+  int64_t out_row_stride;
+};
+
 // Decode family: rows_per_batch <= 32.
 hipError_t launch_decode(const MatArgs& a, hipStream_t stream);
 // MFMA prefill: any rows_per_batch.
 hipError_t launch_prefill(const MatArgs& a, hipStream_t stream);
+// Standalone dequantize / embedding gather.
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 // Min/max group quantizer.
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 

@@ -161,6 +161,24 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
                        int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
                        const int32_t* expert_index, void* y, const qmm_tensor_desc_t* y_desc, void* stream);
 
+/* Dequantize a whole quantized weight to a dense matrix: out[n, k] = RNE_dtype(fl32(fma(s, q, b)))
+ * with s, b the (n, k / group_size) scale and bias and q the code (transformers issue 47331,
+ * "Root cause": the probe dequantizes the packed weight back to a dense tensor; the
+ * float32 multiply-add followed by one rounding to dtype is this library's reading).
+ * out: DEVICE [N, out_row_stride] of dtype, 16-byte aligned, out_row_stride >= K and a
+ * multiple of 8.  w_packed and w_row_stride aligned to a 32-code run: 4 words (16 bytes)
+ * for 4- and 8-bit codes, 2 words for 2- and 6-bit codes, 1 word otherwise.
+ * N == 0 is a no-op. */
+int32_t qmm_dequantize(const qmm_weight_desc_t* w, void* out, int64_t out_row_stride, void* stream);
+
+/* Quantized embedding lookup: out[r, :] = dequantized row indices[r] of W (same rounding as
+ * qmm_dequantize; Metal Kernel Bits=8 final report, section 3.2, dequantizes single rows of
+ * a quantized table).  indices: DEVICE int32 [count]; an index outside [0, N) yields a NaN
+ * row (nothing is read outside the table).  out as for qmm_dequantize with count rows.
+ * count == 0 is a no-op. */
+int32_t qmm_embedding(const qmm_weight_desc_t* w, const int32_t* indices, int64_t count, void* out,
+                      int64_t out_row_stride, void* stream);
+
 /* Host-only: validate a qmv (entry = 0) or qmm_t (entry = 1) call and report its plan
  * without touching the GPU.  Pointers inside `w` are only checked for NULL/alignment when
  * they are non-NULL (pass NULLs to test layouts alone).  Returns QMM_OK or the same error

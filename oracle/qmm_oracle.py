@@ -314,3 +314,34 @@ def gather_reference(x_rows, experts, index, k_cols: int, group_size: int, bits:
             y_ref[r] = one["y_ref"][0]
             tol[r] = one["tol"][0]
     return {"y_ref": y_ref, "tol": tol}
+
+
+# ----------------------------------------------------------------------------------
+# dequantization to the storage dtype, embedding rows
+# ----------------------------------------------------------------------------------
+def dequantize_dtype(codes, scales_bits, biases_bits, group_size: int, dtype: str) -> np.ndarray:
+    """Dense dtype weight ([issue-47331] "Root cause": the probe dequantizes back to a dense
+    tensor).  Reading taken: one float32 multiply-add then one rounding to dtype, i.e.
+    RNE_dtype(RNE_f32(s~ * q + b~)).  s~ * q + b~ is exact in float64 (dequant), and
+    numpy's float64 -> float32 cast rounds to nearest even, so the float32 step is that
+    single rounding.  Returns the dtype bit patterns."""
+    exact = dequant(codes, scales_bits, biases_bits, group_size, dtype)
+    return to_dtype_bits(exact.astype(np.float32), dtype)
+
+
+def embedding_reference(w_packed, scales_bits, biases_bits, indices, k_cols: int, group_size: int,
+                        bits: int, dtype: str):
+    """Rows indices[r] of the dequantized table, as dtype bit patterns; rows whose index is
+    outside [0, N) are None (the library writes NaN there)."""
+    w_packed = np.asarray(w_packed)
+    n_rows = w_packed.shape[0]
+    out = []
+    for i in np.asarray(indices):
+        i = int(i)
+        if 0 <= i < n_rows:
+            codes = unpack(w_packed[i:i + 1], bits, k_cols)
+            out.append(dequantize_dtype(codes, np.asarray(scales_bits)[i:i + 1], np.asarray(biases_bits)[i:i + 1],
+                                        group_size, dtype)[0])
+        else:
+            out.append(None)
+    return out

@@ -80,3 +80,44 @@ def test_gather_qmv_errors():
         q.gather_qmv(buf[0], ex, idx)
     y = torch.zeros(0, 64, dtype=torch.bfloat16, device=dev)
     q.gather_qmv(x[:0], ex, idx[:0], out=y)    # zero rows: no-op
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_dequantize_bit_exact(bits, dtype):
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    for gs, n, k in ((32, 37, 96), (64, 130, 320), (128, 5, 1024)):
+        w = synth.normal_weight(n, k, 0.02, seed=800 + bits + gs).numpy()
+        qz = O.quantize(w, gs, bits, dtype)
+        qw = upload_oracle_weight(qz, dev)
+        out = torch.full((n, k + 8), float("nan"), dtype=TORCH_DTYPE[dtype], device=dev)
+        q.dequantize(qw, out=out[:, :k])
+        torch.cuda.synchronize()
+        expect = O.dequantize_dtype(qz["codes"], qz["scales_bits"], qz["biases_bits"], gs, dtype)
+        got = half_bits(out)
+        assert np.array_equal(got[:, :k], expect), (bits, gs, dtype)
+        assert np.isnan(values(out[:, k:])).all()   # the row padding is untouched
+
+
+@pytest.mark.parametrize("bits,dtype", [(4, "bf16"), (8, "fp16"), (3, "bf16")])
+def test_embedding_rows_bit_exact_and_bad_indices(bits, dtype):
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, k, gs = 300, 256, 64
+    w = synth.normal_weight(n, k, 0.5, seed=900 + bits).numpy()
+    qz = O.quantize(w, gs, bits, dtype)
+    qw = upload_oracle_weight(qz, dev)
+    idx_list = [5, 299, 0, 5, 300, -1, 123]
+    idx = torch.tensor(idx_list, dtype=torch.int32, device=dev)
+    out = q.embedding(qw, idx)
+    torch.cuda.synchronize()
+    rows = O.embedding_reference(O.pack(qz["codes"], bits), qz["scales_bits"], qz["biases_bits"], idx_list, k, gs,
+                                 bits, dtype)
+    got = half_bits(out)
+    for r, ref in enumerate(rows):
+        if ref is None:
+            assert np.isnan(values(out[r])).all(), r
+        else:
+            assert np.array_equal(got[r], ref), r
+    assert q.embedding(qw, idx[:0]).shape == (0, k)

@@ -45,3 +45,39 @@ def test_gather_out_of_range_rows_are_nan():
     g = O.gather_reference(x, [t, t], np.array([-1, 1, 2]), 32, 32, 2, "bf16")
     assert np.isnan(g["y_ref"][0]).all() and np.isnan(g["y_ref"][2]).all()
     assert np.isfinite(g["y_ref"][1]).all()
+
+
+def test_dequantize_dtype_on_grid_is_exact():
+    # power-of-two scales, on-grid biases: every dequantized value is exact in both dtypes
+    rng = np.random.default_rng(10)
+    for dtype in ("bf16", "fp16"):
+        codes = rng.integers(0, 16, size=(3, 64))
+        s = np.array([[2.0 ** -6, 2.0 ** -3]] * 3)
+        b = np.array([[-0.25, 0.5]] * 3)
+        got = O.from_dtype_bits(O.dequantize_dtype(codes, O.to_dtype_bits(s, dtype), O.to_dtype_bits(b, dtype),
+                                                   32, dtype), dtype)
+        expect = codes * np.repeat(s, 32, axis=1) + np.repeat(b, 32, axis=1)
+        assert np.array_equal(got, expect)
+
+
+def test_dequantize_dtype_within_rounding_of_exact():
+    # against the exact float64 dequantization: at most half a float32 step plus half a
+    # dtype step away (two roundings)
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((6, 256)).astype(np.float32)
+    for dtype in ("bf16", "fp16"):
+        qz = O.quantize(w, 64, 5, dtype)
+        exact = O.dequant(qz["codes"], qz["scales_bits"], qz["biases_bits"], 64, dtype)
+        got = O.from_dtype_bits(O.dequantize_dtype(qz["codes"], qz["scales_bits"], qz["biases_bits"], 64, dtype),
+                                dtype)
+        f32_half = np.abs(exact) * 2.0 ** -24
+        assert np.all(np.abs(got - exact) <= 0.5 * O.ulp(exact, dtype) + f32_half + 1e-300)
+
+
+def test_embedding_integer_rows():
+    rng = np.random.default_rng(12)
+    codes, t = _int_expert(rng, 9, 64, 4)
+    rows = O.embedding_reference(*t, [4, 0, 8, 4, 9, -2], 64, 32, 4, "bf16")
+    assert rows[4] is None and rows[5] is None
+    for r, i in zip(rows[:4], [4, 0, 8, 4]):
+        assert np.array_equal(O.from_dtype_bits(r, "bf16"), codes[i].astype(np.float64))
