@@ -134,6 +134,31 @@ def gather_qmv(x: torch.Tensor, experts: ExpertWeights, expert_index: torch.Tens
     return y
 
 
+def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, workspace=None):
+    """Decode qmv with a fused per-row argmax (qmm_qmv_argmax).  Returns (index int32 [rows],
+    value float32 [rows], y or None); with logits=False the logits are not written."""
+    lib = _lib.load()
+    rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
+    y = torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device) if logits else None
+    shape = list(x.shape[:-1]) + [qw.N]
+    strides, acc = [], 1
+    for s in reversed(shape):
+        strides.insert(0, acc)
+        acc *= s
+    yd = _lib.tensor_desc(shape, strides)
+    idx = torch.empty(rows, dtype=torch.int32, device=x.device)
+    val = torch.empty(rows, dtype=torch.float32, device=x.device)
+    ws = workspace if workspace is not None else torch.empty(rows, dtype=torch.int64, device=x.device)
+    assert ws.numel() * ws.element_size() >= 8 * rows
+    if x.dtype != qw.dtype:
+        raise _lib.QmmError(-2, "x, scales and biases must share one dtype")
+    xd = _lib.tensor_desc(x.shape, x.stride())
+    _lib.check(lib.qmm_qmv_argmax(x.data_ptr(), ctypes.byref(xd), ctypes.byref(qw.desc()),
+                                  y.data_ptr() if y is not None else None, ctypes.byref(yd), idx.data_ptr(),
+                                  val.data_ptr(), ws.data_ptr(), _stream(x.device)))
+    return idx, val, y
+
+
 def dequantize(qw: QuantizedWeight, out=None) -> torch.Tensor:
     """Dense [N, K] dtype matrix of the quantized weight (qmm_dequantize)."""
     lib = _lib.load()

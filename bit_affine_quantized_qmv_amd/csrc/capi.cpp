@@ -90,6 +90,29 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
   return launch_status(qmm::launch_decode(a, (hipStream_t)stream));
 }
 
+int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                       const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
+                       void* stream) {
+  std::string err;
+  qmm_plan_t p;
+  // y may be NULL (no logits stored); validate the call with a stand-in output pointer
+  static char y_stand_in alignas(16);
+  int rc = qmm::plan_matmul(x, x_desc, w, y ? y : (void*)&y_stand_in, y_desc, 0, 0, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0) return finish(QMM_OK, "");
+  if (!out_index || !workspace) return finish(QMM_ERR_NULL, "qmv_argmax: out_index and workspace must be non-NULL");
+  if ((uintptr_t)workspace % 8 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
+    return finish(QMM_ERR_ALIGN, "qmv_argmax: workspace must be 8-byte, out_index/out_value 4-byte aligned");
+  if (w->N == 0 || w->N >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "qmv_argmax: need 0 < N < 2^31");
+  qmm::MatArgs a = make_args(x, p, w, y);
+  a.argmax_keys = (unsigned long long*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = qmm::launch_argmax_init(a.argmax_keys, p.rows, s);
+  if (e == hipSuccess) e = qmm::launch_decode(a, s);
+  if (e == hipSuccess) e = qmm::launch_argmax_finish(a.argmax_keys, p.rows, out_index, out_value, s);
+  return launch_status(e);
+}
+
 // Shared validation of the whole-row dequantization entry points.
 static int32_t run_dequant(const qmm_weight_desc_t* w, const int32_t* index, int64_t rows, void* out,
                            int64_t out_row_stride, void* stream) {

@@ -421,6 +421,54 @@ __device__ inline WeightBase weight_base(const MatArgs& a, int64_t z) {
   return r;
 }
 
+// ---- fused argmax.  A key orders (value, column) pairs: the value's float32 bits mapped to
+// an unsigned order (NaN above everything) in the high half, the complement of the column in
+// the low half, so the largest key is the largest value and, among equal values, the
+// smallest column -- the first maximum, as an argmax returns it.
+__device__ inline unsigned long long argmax_key(float v, int64_t n) {
+  uint32_t b = __float_as_uint(v);
+  if (v != v) b = 0x7FC00000u;
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)n);
+}
+
+// Fold one tile's values (rows mt*16 + 4*lg + r, column n) into the lane's running keys;
+// the value is the one stored in y (rounded to the output dtype).
+template <class T, int MT>
+__device__ inline void argmax_update(unsigned long long (&best)[MT][4], const f32x4 (&acc)[MT], int64_t n,
+                                     bool valid) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const unsigned long long k = argmax_key(T::to_f32(T::from_f32(acc[mt][r])), n);
+      best[mt][r] = (valid && k > best[mt][r]) ? k : best[mt][r];
+    }
+}
+
+__device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, mask), hi = __shfl_xor((uint32_t)(v >> 32), mask);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Reduce the wave's keys over the 16 columns of each lane group and merge them into the
+// workgroup's LDS keys `kl` (MROWS entries).
+template <int MT>
+__device__ inline void argmax_merge_wave(unsigned long long (&best)[MT][4], unsigned long long* kl, int lg, int col) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      unsigned long long k = best[mt][r];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const unsigned long long o = shfl_xor_u64(k, m);
+        k = o > k ? o : k;
+      }
+      if (col == 0) atomicMax(&kl[mt * 16 + 4 * lg + r], k);
+    }
+}
+
 template <int MT>
 __device__ inline void poison(f32x4 (&acc)[MT]) {
 #pragma unroll

@@ -88,6 +88,10 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   const int nit = K / S::kSpan;              // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
   uint16_t* ys = (uint16_t*)(sxs + (K / GS + kSxPad) * MROWS) + wave * MROWS * kYRow;
+  // fused argmax: per-row keys of the workgroup, after the store staging area
+  unsigned long long* kl = (unsigned long long*)(ys - wave * MROWS * kYRow + (kYLds ? kStreamWaves * MROWS * kYRow : 0));
+  const bool do_argmax = a.argmax_keys != nullptr;
+  const bool store_y = a.y != nullptr;
   const bool y_vec = (N & 7) == 0 && ((uintptr_t)yb & 15) == 0;
 
   int gword = 0;
@@ -186,6 +190,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
   }
   zero_sx_pad<MT>(sxs, K / GS, tid);
+  if (do_argmax && tid < MROWS) kl[tid] = 0ull;
   lds_barrier();
   sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
   lds_barrier();
@@ -198,8 +203,14 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   for (int j = 0; j < D; ++j) issue_w(j, D + j);
   w_next();
   __builtin_amdgcn_sched_barrier(0);
-  if (t_end <= t_begin) return;
+  // (waves without tiles still take part in the argmax barrier below)
+  if (t_end <= t_begin && !do_argmax) return;
 
+  unsigned long long best[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) best[mt][r] = 0ull;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[TN][MT], part[TN][MT];
 #pragma unroll
@@ -244,7 +255,15 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
 #pragma unroll
         for (int t = 0; t < TN; ++t) poison<MT>(acc[t]);
       }
-      if (kYLds && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
+      if (do_argmax) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const int64_t n = (c_p + t) * 16 + col;
+          argmax_update<T, MT>(best, acc[t], n, c_p + t < t_end && n < N);
+        }
+      }
+      if (!store_y) {
+      } else if (kYLds && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
         store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
       } else {
 #pragma unroll
@@ -264,6 +283,11 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     sub_block(0, scA, biA, scB, biB);
     if (i + 1 < nsub) sub_block(D, scB, biB, scA, biA);
   }
+  if (do_argmax) {
+    argmax_merge_wave<MT>(best, kl, lg, col);
+    lds_barrier();
+    if (tid < rows) atomicMax(&a.argmax_keys[z * rows + tid], kl[tid]);
+  }
 }
 
 template <class T, int BITS, int GS, int MT, int TN>
@@ -273,6 +297,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   constexpr int KC = kChunkXBytes / (MROWS * 2);
   __shared__ u32x4 xs[kChunkXBytes / 16];
   __shared__ float sxs[(KC / 32 + kSxPad) * MROWS];
+  __shared__ unsigned long long kl[MROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -351,8 +376,24 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) poison<MT>(acc[t]);
   }
+  if (a.y) {
 #pragma unroll
-  for (int t = 0; t < TN; ++t) store_tile<T, MT>(acc[t], yb, rows, nrow[t], N, lg);
+    for (int t = 0; t < TN; ++t) store_tile<T, MT>(acc[t], yb, rows, nrow[t], N, lg);
+  }
+  if (a.argmax_keys) {
+    unsigned long long best[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) best[mt][r] = 0ull;
+#pragma unroll
+    for (int t = 0; t < TN; ++t) argmax_update<T, MT>(best, acc[t], nrow[t], nrow[t] < N);
+    if (tid < MROWS) kl[tid] = 0ull;
+    lds_barrier();
+    argmax_merge_wave<MT>(best, kl, lg, col);
+    lds_barrier();
+    if (tid < rows) atomicMax(&a.argmax_keys[z * rows + tid], kl[tid]);
+  }
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -422,7 +463,8 @@ hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
 
 template <int MT, int GS>
 constexpr int stream_lds_bytes(int K) {
-  return 16 * MT * K * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0);
+  return 16 * MT * K * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0) +
+         16 * MT * 8;
 }
 
 template <class T, int BITS, int GS>

@@ -161,6 +161,21 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
                        int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
                        const int32_t* expert_index, void* y, const qmm_tensor_desc_t* y_desc, void* stream);
 
+/* Decode form with a fused per-row argmax (e.g. greedy next-token choice on lm_head logits;
+ * the failure the transformers issue 47331 report shows is this argmax collapsing to
+ * token 0 for every row after the first, section "Reproduction"):
+ *   y = x . dequant(W)^T as in qmv, and for every activation row m
+ *   out_index[m] = the first n with y[m, n] == max_n y[m, n], out_value[m] = that value
+ *   (as float32; NaN counts as larger than any number).
+ * The comparison uses the values y holds (rounded to dtype), so out_index equals an argmax
+ * over the returned logits.  y may be NULL: the logits are then not written at all.
+ * workspace: DEVICE, 8-byte aligned, 8 bytes per activation row (overwritten).  out_value may
+ * be NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows); 0 < N < 2^31.
+ * Three kernels are enqueued: key initialisation, the decode kernel, key read-out. */
+int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                       const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
+                       void* stream);
+
 /* Dequantize a whole quantized weight to a dense matrix: out[n, k] = RNE_dtype(fl32(fma(s, q, b)))
  * with s, b the (n, k / group_size) scale and bias and q the code (transformers issue 47331,
  * "Root cause": the probe dequantizes the packed weight back to a dense tensor; the

@@ -345,3 +345,17 @@ def embedding_reference(w_packed, scales_bits, biases_bits, indices, k_cols: int
         else:
             out.append(None)
     return out
+
+
+# ----------------------------------------------------------------------------------
+# per-row argmax of the logits
+# ----------------------------------------------------------------------------------
+def argmax_acceptable(y_ref, tol) -> list:
+    """Indices a correct fused argmax may return for each row: every column whose exact
+    value could be the largest once each value is allowed its tolerance, i.e.
+    y_ref[n] + tol[n] >= max_j (y_ref[j] - tol[j]).  (Several answers are correct when
+    logits lie within the tolerance of each other.)"""
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    tol = np.asarray(tol, dtype=np.float64)
+    floor = (y_ref - tol).max(axis=1, keepdims=True)
+    return [set(np.nonzero(row)[0].tolist()) for row in (y_ref + tol >= floor)]

@@ -121,3 +121,81 @@ def test_embedding_rows_bit_exact_and_bad_indices(bits, dtype):
         else:
             assert np.array_equal(got[r], ref), r
     assert q.embedding(qw, idx[:0]).shape == (0, k)
+
+
+@pytest.mark.parametrize("m,n,bits,dtype", [(32, 3001, 4, "bf16"), (5, 777, 8, "fp16"), (17, 130, 3, "bf16")])
+def test_qmv_argmax_parity(m, n, bits, dtype):
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    k, gs = 1024, 64
+    w = synth.normal_weight(n, k, 0.02, seed=1000 + n).numpy()
+    qz = O.quantize(w, gs, bits, dtype)
+    qw = upload_oracle_weight(qz, dev)
+    x = synth.normal_x((m, k), dtype, seed=1001).to(dev)
+    idx, val, y = q.qmv_argmax(x, qw)
+    idx2, val2, none = q.qmv_argmax(x, qw, logits=False)
+    y_plain = q.qmv(x, qw)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))     # same logits as qmv
+    assert torch.equal(idx, idx2) and torch.equal(val, val2)               # logits optional
+    first = torch.argmax(y.float(), dim=1).to(torch.int32)                 # first maximum
+    assert torch.equal(idx, first)
+    assert torch.equal(val, y.float().gather(1, idx.long()[:, None])[:, 0])
+    ref = O.reference(values(x), O.pack(qz["codes"], bits), qz["scales_bits"], qz["biases_bits"], k, gs, bits, dtype)
+    ok = O.argmax_acceptable(ref["y_ref"], ref["tol"])
+    for r in range(m):
+        assert int(idx[r]) in ok[r], r
+
+
+def test_qmv_argmax_ties_pick_first_and_nan():
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, k, gs, bits, dtype = 300, 512, 64, 4, "bf16"
+    w = synth.normal_weight(n, k, 0.02, seed=1100).numpy()
+    for r in (41, 7, 250):         # three identical, dominant rows: 7 must win
+        w[r] = 1.0 + 0.01 * np.arange(k) / k
+    qw = upload_oracle_weight(O.quantize(w, gs, bits, dtype), dev)
+    x = torch.ones(3, k, dtype=torch.bfloat16, device=dev)
+    x[2, 5] = float("nan")         # a NaN row: every logit NaN, the first one wins
+    idx, val, y = q.qmv_argmax(x, qw)
+    torch.cuda.synchronize()
+    assert idx[:2].tolist() == [7, 7]
+    assert int(idx[2]) == 0 and bool(torch.isnan(val[2]))
+
+
+def test_qmv_argmax_lm_head_full_size():
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    c = synth.LM_HEAD
+    w = synth.normal_weight(c["n"], c["k"], c["w_std"], seed=c["w_seed"]).to(dev)
+    qw = q.quantize(w, c["group_size"], c["bits"], c["dtype"])
+    x = synth.normal_x((c["m"], c["k"]), c["dtype"], seed=c["x_seed"]).to(dev)
+    idx, val, y = q.qmv_argmax(x, qw)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, torch.argmax(y.float(), dim=1).to(torch.int32))
+    # the chosen columns against the oracle, one by one
+    rows = sorted(set(idx.tolist()))
+    from qmm_testlib import reference_rows
+    ref = reference_rows(values(x), qw, c["dtype"], rows=rows)
+    for r in range(c["m"]):
+        j = rows.index(int(idx[r]))
+        assert abs(float(val[r]) - ref["y_ref"][r, j]) <= ref["tol"][r, j]
+
+
+def test_qmv_argmax_chunked_activations():
+    # 20 rows x K = 4096 do not fit in LDS at once: the chunked decode kernel runs
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, k, gs, bits, dtype = 1500, 4096, 128, 4, "bf16"
+    w = synth.normal_weight(n, k, 0.02, seed=1200).numpy()
+    qz = O.quantize(w, gs, bits, dtype)
+    qw = upload_oracle_weight(qz, dev)
+    x = synth.normal_x((20, k), dtype, seed=1201).to(dev)
+    idx, val, y = q.qmv_argmax(x, qw)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, torch.argmax(y.float(), dim=1).to(torch.int32))
+    ref = O.reference(values(x), O.pack(qz["codes"], bits), qz["scales_bits"], qz["biases_bits"], k, gs, bits, dtype)
+    assert_close(y, ref, "chunked qmv")
+    ok = O.argmax_acceptable(ref["y_ref"], ref["tol"])
+    assert all(int(idx[r]) in ok[r] for r in range(20))

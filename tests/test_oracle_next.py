@@ -81,3 +81,13 @@ def test_embedding_integer_rows():
     assert rows[4] is None and rows[5] is None
     for r, i in zip(rows[:4], [4, 0, 8, 4]):
         assert np.array_equal(O.from_dtype_bits(r, "bf16"), codes[i].astype(np.float64))
+
+
+def test_argmax_acceptable_exact_and_ties():
+    # exact integer logits (tolerance 0): the unique maximum, or every tied maximum
+    y = np.array([[1.0, 5.0, 3.0, 5.0], [-2.0, -1.0, -3.0, -1.5]])
+    got = O.argmax_acceptable(y, np.zeros_like(y))
+    assert got == [{1, 3}, {1}]
+    # tolerance widens the set to the values that could overtake the maximum
+    got = O.argmax_acceptable(y, np.full_like(y, 0.3))
+    assert got == [{1, 3}, {1, 3}]
