@@ -182,8 +182,10 @@ def embedding(qw: QuantizedWeight, indices: torch.Tensor, out=None) -> torch.Ten
 
 
 def plan(x_shape, x_stride, N: int, K: int, group_size: int = 64, bits: int = 4,
-         dtype: int = _lib.QMM_BF16, entry: int = 1, flags: int = 0, y_shape=None, y_stride=None) -> dict:
-    """Host-only dispatcher query (qmm_plan): the plan, or QmmError."""
+         dtype: int = _lib.QMM_BF16, entry: int = 1, flags: int = 0, y_shape=None, y_stride=None,
+         w_row_stride=None) -> dict:
+    """Host-only dispatcher query (qmm_plan): the plan, or QmmError.  The weight row stride
+    defaults to the packed row padded to a multiple of 4 words."""
     lib = _lib.load()
     if y_shape is None:
         y_shape = list(x_shape[:-1]) + [N]
@@ -195,7 +197,7 @@ def plan(x_shape, x_stride, N: int, K: int, group_size: int = 64, bits: int = 4,
     xd = _lib.tensor_desc(x_shape, x_stride)
     yd = _lib.tensor_desc(y_shape, y_stride)
     wd = _lib.WeightDesc()
-    wd.w_row_stride = K * bits // 32 + (-(K * bits // 32)) % 4
+    wd.w_row_stride = K * bits // 32 + (-(K * bits // 32)) % 4 if w_row_stride is None else w_row_stride
     wd.sb_row_stride = K // group_size
     wd.N, wd.K, wd.group_size, wd.bits, wd.dtype = N, K, group_size, bits, dtype
     p = _lib.Plan()

@@ -60,7 +60,6 @@ int plan_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_des
                                    (long long)K, (long long)N);
   if (K % w->group_size) return fail(err, QMM_ERR_SHAPE, "K=%lld is not a multiple of group_size=%d",
                                      (long long)K, w->group_size);
-  if (K % 128) return fail(err, QMM_ERR_ALIGN, "K=%lld must be a multiple of 128", (long long)K);
   if (K > (1ll << 30) || N > (1ll << 40))
     return fail(err, QMM_ERR_SHAPE, "K=%lld or N=%lld too large", (long long)K, (long long)N);
   if (xd->ndim < 1 || xd->ndim > QMM_MAX_DIMS)
@@ -95,9 +94,12 @@ int plan_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_des
   if (w->w_row_stride < row_words)
     return fail(err, QMM_ERR_SHAPE, "w_row_stride=%lld < K*bits/32=%lld", (long long)w->w_row_stride,
                 (long long)row_words);
-  if (w->w_row_stride % 4)
-    return fail(err, QMM_ERR_ALIGN, "w_row_stride=%lld must be a multiple of 4 words",
-                (long long)w->w_row_stride);
+  // rows are read in 32-code runs: 4 words (16 bytes) for 4/8-bit codes, 2 words for
+  // 2/6-bit codes, single words otherwise
+  const int run_align = w->bits % 4 == 0 ? 4 : (w->bits % 2 == 0 ? 2 : 1);
+  if (w->w_row_stride % run_align)
+    return fail(err, QMM_ERR_ALIGN, "w_row_stride=%lld must be a multiple of %d words for %d-bit codes",
+                (long long)w->w_row_stride, run_align, w->bits);
   if (w->sb_row_stride < n_groups)
     return fail(err, QMM_ERR_SHAPE, "sb_row_stride=%lld < K/group_size=%lld", (long long)w->sb_row_stride,
                 (long long)n_groups);
@@ -110,7 +112,11 @@ int plan_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_des
   p.batches = 1;
   p.rows_per_batch = M;
   p.seg_rows = M > 0 ? M : 1;
-  p.family = M <= QMM_DECODE_MAX_ROWS ? 0 : 1;
+  // The decode kernels take K a multiple of 128 and rows that start on 16-byte boundaries;
+  // other shapes (any K that is a multiple of the group size) go through the MFMA kernel at
+  // every row count: its partial last k step is masked, and its per-row arithmetic does not
+  // depend on the row count either.
+  p.family = (M <= QMM_DECODE_MAX_ROWS && K % 128 == 0 && w->w_row_stride % 4 == 0) ? 0 : 1;
   if (entry == 0 && M > QMM_DECODE_MAX_ROWS)
     return fail(err, QMM_ERR_SHAPE, "qmv takes at most %d activation rows, got %lld; use qmm_t",
                 QMM_DECODE_MAX_ROWS, (long long)M);

@@ -65,26 +65,35 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs 
     const int64_t m = bm0 + ar[i];
     const int64_t mr = m < rows ? m : 0;
     amask[i] = m < rows ? 0xFFFFFFFFu : 0u;
-    arow[i] = xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride + 8 * ac[i];
+    arow[i] = xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride;
   }
   // weight: thread -> row wr, 32-code half wh of the 64 k of a step
   const int wr = tid >> 1, wh = tid & 1;
   const int64_t wn_row = bn0 + wr < N ? bn0 + wr : N - 1;
-  const uint32_t* wrow = a.w + wn_row * a.w_row_stride + wh * BITS;
+  const uint32_t* wrow = a.w + wn_row * a.w_row_stride;
   const uint16_t* srow = (const uint16_t*)a.scales + wn_row * a.sb_row_stride;
   const uint16_t* brow = (const uint16_t*)a.biases + wn_row * a.sb_row_stride;
 
   u32x4 ra[A_PER];
   uint32_t rw[BITS];
   uint32_t rs = 0, rb = 0;
+  // When K is not a multiple of BK the last step is partial: activation chunks and code
+  // runs at k >= K read the row's first chunk / run instead and are zeroed (K is a multiple
+  // of 32, so a chunk or run is either wholly inside or wholly outside the row).
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) ra[i] = *(const u32x4*)(arow[i] + k0) & amask[i];
-    load_codes<BITS>(rw, wrow + kt * (BK * BITS / 32));
-    const int g = (k0 + 32 * wh) / gs;
-    rs = srow[g];
-    rb = brow[g];
+    for (int i = 0; i < A_PER; ++i) {
+      const int k = k0 + 8 * ac[i];
+      const bool kv = k < K;
+      ra[i] = *(const u32x4*)(arow[i] + (kv ? k : 0)) & (kv ? amask[i] : 0u);
+    }
+    const int kw = k0 + 32 * wh;
+    const bool wv_ok = kw < K;
+    load_codes<BITS>(rw, wrow + (wv_ok ? kw / 32 * BITS : 0));
+    const int g = wv_ok ? kw / gs : 0;
+    rs = wv_ok ? srow[g] : 0u;
+    rb = wv_ok ? brow[g] : 0u;
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -107,10 +116,10 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs 
   // buffer, interleaved with the first half of the MFMAs; the loads of step kt+2 are then
   // issued into the freed registers.  One barrier per step.  The body has no branches: the
   // last step reloads a clamped step and writes it into the buffer no one reads any more.
-  const int nk = K / BK;   // >= 2 (K is a multiple of 128)
+  const int nk = (K + BK - 1) / BK;
   gload(0);
   lstore(0);
-  gload(1);
+  gload(nk > 1 ? 1 : 0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
@@ -187,7 +196,7 @@ hipError_t launch_dtype(const MatArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const MatArgs& a, hipStream_t stream) {
-  if (a.rows_per_batch <= 0 || a.batches > 65535 || a.K % BK != 0) return hipErrorInvalidValue;
+  if (a.rows_per_batch <= 0 || a.batches > 65535 || a.K % 32 != 0) return hipErrorInvalidValue;
   return a.dtype == 1 ? launch_dtype<Bf16>(a, stream) : launch_dtype<Fp16>(a, stream);
 }
 

@@ -130,15 +130,22 @@ int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride,
  * Sums of x are taken in float32 after widening each element (MLX pull request 4516,
  * first commit: widen each input before adding it to the bias * sum(x) term).
  * Alignment: x, w_packed 16-byte aligned; x strides (except the last) multiples of 8;
- * w_row_stride a multiple of 4; K a multiple of 128.
+ * w_row_stride a multiple of the 32-code run: 4 words for 4- and 8-bit codes, 2 words for
+ * 2- and 6-bit codes, 1 word otherwise.
+ * Any K that is a multiple of group_size is accepted.  When K is a multiple of 128 and
+ * w_row_stride a multiple of 4 words the decode kernels run; otherwise (e.g. K = 96 with
+ * group_size 32, or rows padded to an odd word count) the call runs the MFMA kernel that
+ * qmm_t uses for many rows, whose last k step is masked (MLX pull request 4516, second commit text: inputs that
+ * are not aligned for the fast qmv kernel take the generic kernel and its guarded tail).
  * M == 0 or N == 0 is a no-op returning QMM_OK. */
 int32_t qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
             void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
 
 /* Transposed matrix-matrix form (prefill and batched decode): same operation and contract
  * as qmv, any number of rows.  Up to QMM_DECODE_MAX_ROWS collapsed rows it runs the same
- * kernels as qmv (so the results agree bitwise); beyond that it runs the MFMA prefill
- * kernel, which dequantizes weight tiles to dtype in LDS before the products. */
+ * kernels as qmv (so the results agree bitwise); beyond that, and at every row count for the
+ * shapes the decode kernels do not take, it runs the MFMA prefill kernel, which dequantizes
+ * weight tiles to dtype in LDS before the products. */
 int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
               void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
 
@@ -156,7 +163,9 @@ int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_d
  * stack).  Each row runs the decode kernels on its own (at most 65535 rows), and its result
  * is bit-identical to qmv on that row with expert e's weight.
  * Strides: w_expert_stride >= N * w_row_stride (a multiple of 4), sb_expert_stride >=
- * N * sb_row_stride.  Other requirements as for qmv.  Zero rows or N == 0 is a no-op. */
+ * N * sb_row_stride.  K must be a multiple of 128 and w_row_stride of 4 words (the decode
+ * kernels' shapes; QMM_ERR_ALIGN otherwise).  Other requirements as for qmv.  Zero rows or
+ * N == 0 is a no-op. */
 int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
                        int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
                        const int32_t* expert_index, void* y, const qmm_tensor_desc_t* y_desc, void* stream);
@@ -170,7 +179,8 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
  * The comparison uses the values y holds (rounded to dtype), so out_index equals an argmax
  * over the returned logits.  y may be NULL: the logits are then not written at all.
  * workspace: DEVICE, 8-byte aligned, 8 bytes per activation row (overwritten).  out_value may
- * be NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows); 0 < N < 2^31.
+ * be NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows), but K must be a
+ * multiple of 128 and w_row_stride of 4 words (QMM_ERR_ALIGN otherwise); 0 < N < 2^31.
  * Three kernels are enqueued: key initialisation, the decode kernel, key read-out. */
 int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                        const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,

@@ -115,7 +115,6 @@ def test_three_levels_rejected_with_layout_in_message():
 def test_rejections():
     _err([3, K], [K, 2], -4)                       # last-dim stride != 1
     _err([3, K], [-K, 1], -4)                      # negative stride
-    _err([3, 1056], [1056, 1], -5, group_size=32)  # K a multiple of 32, not of 128
     _err([3, 96], [96, 1], -3, group_size=64)      # K not a multiple of group_size
     _err([3, K], [K, 1], -2, bits=7)
     _err([3, K], [K, 1], -2, group_size=16)
@@ -134,6 +133,28 @@ def test_empty_is_a_plan():
     assert p["rows"] == 0
     p = _plan([3, K], [K, 1], N=0)
     assert p["rows"] == 3
+
+
+def test_unaligned_k_and_odd_row_strides_take_the_mfma_kernel():
+    """K a multiple of the group size but not of 128, or weight rows padded to a word count
+    the decode kernels cannot load in 16-byte pieces, plan the MFMA kernel at every row count
+    (MLX pull request 4516, second commit text: unaligned inputs take the generic kernel)."""
+    for m in (1, 7, 32, 33, 500):
+        p = _plan([m, 1056], [1056, 1], group_size=32)
+        assert (p["rows"], p["family"]) == (m, 1)
+        p = _plan([m, 1088], [1088, 1], group_size=64, entry=0 if m <= 32 else 1)
+        assert p["family"] == 1
+        assert _plan([m, K], [K, 1], bits=3, w_row_stride=97)["family"] == 1
+        assert _plan([m, K], [K, 1], bits=3, w_row_stride=100)["family"] == (0 if m <= 32 else 1)
+    assert _plan([4, 32], [32, 1], group_size=32, entry=0)["family"] == 1
+    # the run alignment of each code width: 4 words for 4/8-bit, 2 for 2/6-bit, 1 otherwise
+    _err([3, K], [K, 1], -5, bits=4, w_row_stride=130)
+    _err([3, K], [K, 1], -5, bits=8, w_row_stride=258)
+    _err([3, K], [K, 1], -5, bits=6, w_row_stride=193)
+    _err([3, K], [K, 1], -5, bits=2, w_row_stride=65)
+    assert _plan([3, K], [K, 1], bits=6, w_row_stride=194)["family"] == 1
+    assert _plan([3, K], [K, 1], bits=5, w_row_stride=161)["family"] == 1
+    _err([3, K], [K, 1], -3, bits=5, w_row_stride=159)   # shorter than a row
 
 
 def test_qmv_family_boundary():
