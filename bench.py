@@ -152,6 +152,94 @@ def _oracle_rate(run_sample, budget_s):
     return (done_units / spent if spent > 0 else 0.0), desc, i
 
 
+def _leg(metric, amount, t, bound, unit, peak, kernel, config):
+    """One measured leg: `amount` algorithmic bytes (GB/s legs) or flops (TFLOP/s legs) per call,
+    over the graph-replay step time (value) and the event-timed launch duration (roofline)."""
+    scale = 1e9 if unit == "GB/s" else 1e12
+    value = amount / (t["wall_ms"] * 1e-3) / scale
+    achieved = amount / (t["kernel_mean_ms"] * 1e-3) / scale
+    return {"metric": metric, "value": round(value, 1), "unit": unit, "ms_per_step": round(t["wall_ms"], 5),
+            "config": config,
+            "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                         "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel,
+                         "kernel_ms_mean": round(t["kernel_mean_ms"], 5),
+                         "kernel_ms_median": round(t["kernel_median_ms"], 5)}}
+
+
+def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
+    """Gathered-weight decode, standalone dequantize and the unaligned-K prefill."""
+    # gathered qmv over an expert stack, every expert read once per call
+    ec = synth.EXPERTS
+    e, n, k, bits, gs = ec["e"], ec["n"], ec["k"], ec["bits"], ec["group_size"]
+    we = synth.normal_weight(e * n, k, ec["w_std"], seed=ec["w_seed"])
+    st = q.quantize(we.to(dev), gs, bits, ec["dtype"])
+    del we
+    stacks = []
+    for c in range(3):
+        wp = st.w_packed.view(e, n, -1)
+        sc = st.scales.view(e, n, -1)
+        bi = st.biases.view(e, n, -1)
+        if c:
+            wp, sc, bi = wp.clone(), sc.clone(), bi.clone()
+        stacks.append(q.ExpertWeights(wp, sc, bi, n, k, gs, bits))
+    rows = ec["rows"]
+    gx = [synth.normal_x((rows, k), ec["dtype"], seed=ec["x_seed"] + c).to(dev) for c in range(3)]
+    gi = [synth.permutation(e, ec["idx_seed"] + c)[:rows].contiguous().to(dev) for c in range(3)]
+    gy = [torch.empty(rows, n, dtype=gx[0].dtype, device=dev) for _ in range(3)]
+    expert_bytes = n * k * bits // 8 + 2 * n * (k // gs) * 2
+    gbytes = rows * (expert_bytes + k * 2 + n * 2 + 4)
+    tg = _time_steps(lambda i: q.gather_qmv(gx[i % 3], stacks[i % 3], gi[i % 3], out=gy[i % 3]),
+                     nsteps, nwarm, torch, not args.no_graph)
+    res["gather_qmv"] = _leg(
+        "gathered qmv effective HBM GB/s", gbytes, tg, "hbm", "GB/s", HBM_PEAK_GBS, "qmv decode kernels",
+        {"workload": "gathered qmv: 128 rows x [1,1408] bf16, each against its own expert of a "
+                     "[128,704,1408] 8-bit group 32 bf16 stack (seeded permutation)",
+         "algorithmic_bytes_per_call": gbytes})
+    del stacks, gx, gi, gy, st
+
+    # standalone dequantize of the prefill weight
+    pc = synth.PREFILL
+    pn, pk = pc["n"], pc["k"]
+    pw = synth.normal_weight(pn, pk, pc["w_std"], seed=pc["w_seed"])
+    pq0 = q.quantize(pw.to(dev), pc["group_size"], pc["bits"], pc["dtype"])
+    del pw
+    pqs = [pq0, q.QuantizedWeight(pq0.w_packed.clone(), pq0.scales.clone(), pq0.biases.clone(), pn, pk,
+                                  pc["group_size"], pc["bits"])]
+    douts = [torch.empty(pn, pk, dtype=pq0.dtype, device=dev) for _ in range(2)]
+    dbytes = pn * pk * pc["bits"] // 8 + 2 * pn * (pk // pc["group_size"]) * 2 + pn * pk * 2
+    td = _time_steps(lambda i: q.dequantize(pqs[i % 2], out=douts[i % 2]), nsteps, nwarm, torch,
+                     not args.no_graph)
+    res["dequantize"] = _leg(
+        "dequantize effective HBM GB/s", dbytes, td, "hbm", "GB/s", HBM_PEAK_GBS, "dequant_rows_kernel",
+        {"workload": "dequantize W [14336,4096] 4-bit group 128 bf16 -> dense [14336,4096] bf16",
+         "algorithmic_bytes_per_call": dbytes})
+    del pqs, douts, pq0
+
+    # unaligned K: the prefill shape at K = 4096 + 32 (group 32), and its 32-row decode
+    uc = synth.UNALIGNED
+    un, uk = uc["n"], uc["k"]
+    uw = synth.normal_weight(un, uk, uc["w_std"], seed=uc["w_seed"])
+    uq = q.quantize(uw.to(dev), uc["group_size"], uc["bits"], uc["dtype"])
+    del uw
+    ux = synth.normal_x((uc["b"], uc["s"], uk), uc["dtype"], seed=uc["x_seed"]).to(dev)
+    uy = torch.empty(uc["b"], uc["s"], un, dtype=ux.dtype, device=dev)
+    flops = 2.0 * uc["b"] * uc["s"] * un * uk
+    tu = _time_steps(lambda i: q.qmm_t(ux, uq, out=uy), max(10, nsteps // 2), nwarm, torch, not args.no_graph)
+    res["unaligned_k"] = _leg(
+        "unaligned-K qmm_t TFLOP/s", flops, tu, "mfma", "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "qmm_prefill_kernel",
+        {"workload": "prefill qmm_t at unaligned K: x [4,512,4128] bf16, W [14336,4128] 4-bit group 32 "
+                     "bf16 (last k step of 32)", "flops_per_call": flops})
+    dx = ux[0, :32].contiguous().view(32, 1, uk)
+    dy = torch.empty(32, 1, un, dtype=ux.dtype, device=dev)
+    tdd = _time_steps(lambda i: q.qmv(dx, uq, out=dy), nsteps, nwarm, torch, not args.no_graph)
+    ubytes = un * uk * uc["bits"] // 8 + 2 * un * (uk // uc["group_size"]) * 2 + 32 * uk * 2 + 32 * un * 2
+    res["unaligned_k"]["decode_32_rows"] = {
+        "kernel_ms_mean": round(tdd["kernel_mean_ms"], 5),
+        "effective_GBps": round(ubytes / (tdd["kernel_mean_ms"] * 1e-3) / 1e9, 1),
+        "note": "x [32,1,4128]: runs the MFMA kernel (the decode kernels take K a multiple of 128)"}
+    del uq, ux, uy, dx, dy
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,7 +248,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing per leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["qmv", "qmm_t", "all"], default="all")
+    ap.add_argument("--only", choices=["qmv", "qmm_t", "next", "all"], default="all",
+                    help="legs besides the headline qmv: the prefill qmm_t, the next rows "
+                         "(gathered qmv, fused argmax, dequantize, embedding, unaligned K), or all")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps eagerly instead of replaying them from a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -242,6 +332,42 @@ def main():
                     "pages_apple_m4max_ms": {"batched_grid_z": 60.0, "flattened": 2.2}},
     }
     out["qmv"] = line
+    nsteps = max(10, args.steps // 4)
+    nwarm = max(3, args.warmup // 4)
+    if args.only in ("all", "next"):
+        out["next"] = {}
+        # fused argmax on the lm_head logits, with and without storing them
+        idx = torch.empty(m, dtype=torch.int32, device=dev)
+        val = torch.empty(m, dtype=torch.float32, device=dev)
+        ws = torch.empty(m, dtype=torch.int64, device=dev)
+        arg_rows = {}
+        for logits in (True, False):
+            ta = _time_steps(lambda i: q.qmv_argmax(xs[i % copies], qws[i % copies], logits=logits, workspace=ws,
+                                                    out=ys[i % copies] if logits else None, out_index=idx,
+                                                    out_value=val),
+                             nsteps, nwarm, torch, not args.no_graph)
+            nbytes = qmv_bytes - (0 if logits else m * n * 2) + m * 8
+            arg_rows["with_logits" if logits else "no_logits"] = _leg(
+                "fused argmax effective HBM GB/s", nbytes, ta, "hbm", "GB/s", HBM_PEAK_GBS,
+                "qmv_stream_kernel (+ key init / read-out kernels)",
+                {"workload": "lm_head decode qmv + per-row argmax: x [32,1,1024] bf16, W [151936,1024] "
+                             "4-bit group 64; logits %s" % ("stored" if logits else "not stored"),
+                 "algorithmic_bytes_per_call": nbytes})
+        out["next"]["qmv_argmax"] = arg_rows
+        # quantized embedding gather from the lm_head table
+        ec = synth.EMBED
+        idxs = [synth.token_indices(ec["count"], n, ec["idx_seed"] + c).to(dev) for c in range(copies)]
+        eouts = [torch.empty(ec["count"], k, dtype=x0.dtype, device=dev) for _ in range(copies)]
+        row_bytes = k * bits // 8 + 2 * (k // gs) * 2
+        ebytes = ec["count"] * (row_bytes + k * 2 + 4)
+        te = _time_steps(lambda i: q.embedding(qws[i % copies], idxs[i % copies], out=eouts[i % copies]),
+                         nsteps, nwarm, torch, not args.no_graph)
+        out["next"]["embedding"] = _leg(
+            "quantized embedding gather effective HBM GB/s", ebytes, te, "hbm", "GB/s", HBM_PEAK_GBS,
+            "dequant_rows_kernel",
+            {"workload": "embedding: 2048 seeded token rows of the [151936,1024] 4-bit group 64 bf16 table "
+                         "-> [2048,1024] bf16", "algorithmic_bytes_per_call": ebytes})
+        del idxs, eouts
     del qws, xs, ys, w
 
     # ------------------------------------------------------------ prefill qmm_t
@@ -281,6 +407,9 @@ def main():
                          "kernel_ms_median": round(pt["kernel_median_ms"], 5)},
         }
         del pqs, pxs, pys, buf, pw
+
+    if args.only in ("all", "next"):
+        _next_legs(args, q, torch, dev, synth, out["next"], nsteps, nwarm)
 
     # ------------------------------------------------------------ CPU oracle baselines
     if not args.no_cpu_baseline:
@@ -339,6 +468,8 @@ def main():
     line = out["qmv"]
     if "qmm_t" in out:
         line["qmm_t"] = out["qmm_t"]
+    if "next" in out:
+        line["next_rows"] = out["next"]
     print(json.dumps(line))
 
 

@@ -134,20 +134,30 @@ def gather_qmv(x: torch.Tensor, experts: ExpertWeights, expert_index: torch.Tens
     return y
 
 
-def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, workspace=None):
+def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, workspace=None, out=None,
+               out_index=None, out_value=None):
     """Decode qmv with a fused per-row argmax (qmm_qmv_argmax).  Returns (index int32 [rows],
-    value float32 [rows], y or None); with logits=False the logits are not written."""
+    value float32 [rows], y or None); with logits=False the logits are not written.  `out`,
+    `out_index` and `out_value` optionally supply the output tensors."""
     lib = _lib.load()
     rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
-    y = torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device) if logits else None
+    if not logits:
+        y = None
+    elif out is not None:
+        y = out
+        assert y.dtype == x.dtype and y.is_contiguous() and tuple(y.shape) == tuple(x.shape[:-1]) + (qw.N,)
+    else:
+        y = torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device)
     shape = list(x.shape[:-1]) + [qw.N]
     strides, acc = [], 1
     for s in reversed(shape):
         strides.insert(0, acc)
         acc *= s
     yd = _lib.tensor_desc(shape, strides)
-    idx = torch.empty(rows, dtype=torch.int32, device=x.device)
-    val = torch.empty(rows, dtype=torch.float32, device=x.device)
+    idx = out_index if out_index is not None else torch.empty(rows, dtype=torch.int32, device=x.device)
+    val = out_value if out_value is not None else torch.empty(rows, dtype=torch.float32, device=x.device)
+    assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows
+    assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows
     ws = workspace if workspace is not None else torch.empty(rows, dtype=torch.int64, device=x.device)
     assert ws.numel() * ws.element_size() >= 8 * rows
     if x.dtype != qw.dtype:

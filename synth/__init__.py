@@ -15,6 +15,12 @@ Workloads (shapes of the pages' cases, values synthetic):
            x alternating 2048, 1; codes constructed (see odd_n_weight).
   prefill  x [4,512,4096] ~ N(0,1) (and a view narrowed on dim 1 of [4,1024,4096]),
            W [14336, 4096] ~ N(0, 0.02), 4-bit, group 128, bf16.
+  experts  a stack of 128 experts of [704, 1408], 8-bit, group 32, bf16 (the expert tensor
+           shapes of the Bits=8 report, section 4.3); 128 decode rows, row r routed to
+           expert perm[r] of a seeded permutation, so every expert is read once.
+  embed    the lm_head table [151936, 1024] 4-bit group 64 read as a tied embedding: 2048
+           seeded token indices.
+  unaligned the prefill weight at K = 4128 (4096 + 32), group 32: x [4,512,4128].
 """
 from __future__ import annotations
 
@@ -90,6 +96,23 @@ LM_HEAD = {"n": 151936, "k": 1024, "m": 32, "bits": 4, "group_size": 64, "dtype"
            "w_seed": 300, "x_seed": 301, "w_std": 0.02}
 PREFILL = {"n": 14336, "k": 4096, "b": 4, "s": 512, "bits": 4, "group_size": 128,
            "dtype": "bf16", "w_seed": 500, "x_seed": 501, "buf_seed": 502, "w_std": 0.02}
+
+
+EXPERTS = {"e": 128, "n": 704, "k": 1408, "bits": 8, "group_size": 32, "dtype": "bf16",
+           "rows": 128, "w_seed": 700, "x_seed": 701, "idx_seed": 702, "w_std": 0.02}
+EMBED = {"count": 2048, "idx_seed": 801}
+UNALIGNED = {"n": 14336, "k": 4128, "b": 4, "s": 512, "bits": 4, "group_size": 32,
+             "dtype": "bf16", "w_seed": 900, "x_seed": 901, "w_std": 0.02}
+
+
+def permutation(n: int, seed: int) -> torch.Tensor:
+    """int32 seeded permutation of range(n)."""
+    return torch.randperm(n, generator=_gen(seed)).to(torch.int32)
+
+
+def token_indices(count: int, n: int, seed: int) -> torch.Tensor:
+    """int32 [count] uniform in [0, n)."""
+    return torch.randint(0, n, (count,), generator=_gen(seed), dtype=torch.int64).to(torch.int32)
 
 
 def rows_sample(n: int, count: int, seed: int) -> np.ndarray:
