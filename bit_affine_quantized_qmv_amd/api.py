@@ -134,11 +134,18 @@ def gather_qmv(x: torch.Tensor, experts: ExpertWeights, expert_index: torch.Tens
     return y
 
 
+def argmax_workspace(rows: int, device) -> torch.Tensor:
+    """A zero-filled workspace for qmv_argmax calls of up to `rows` activation rows; every call
+    leaves it zero again, so it can be kept and reused in stream order."""
+    return torch.zeros(rows + 1, dtype=torch.int64, device=device)
+
+
 def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, workspace=None, out=None,
                out_index=None, out_value=None):
     """Decode qmv with a fused per-row argmax (qmm_qmv_argmax).  Returns (index int32 [rows],
     value float32 [rows], y or None); with logits=False the logits are not written.  `out`,
-    `out_index` and `out_value` optionally supply the output tensors."""
+    `out_index` and `out_value` optionally supply the output tensors; `workspace` is one from
+    argmax_workspace (a fresh one is allocated when None)."""
     lib = _lib.load()
     rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
     if not logits:
@@ -158,8 +165,8 @@ def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, worksp
     val = out_value if out_value is not None else torch.empty(rows, dtype=torch.float32, device=x.device)
     assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows
     assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows
-    ws = workspace if workspace is not None else torch.empty(rows, dtype=torch.int64, device=x.device)
-    assert ws.numel() * ws.element_size() >= 8 * rows
+    ws = workspace if workspace is not None else argmax_workspace(rows, x.device)
+    assert ws.is_contiguous() and ws.numel() * ws.element_size() >= 8 * (rows + 1)
     if x.dtype != qw.dtype:
         raise _lib.QmmError(-2, "x, scales and biases must share one dtype")
     xd = _lib.tensor_desc(x.shape, x.stride())

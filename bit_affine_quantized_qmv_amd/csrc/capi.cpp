@@ -110,11 +110,10 @@ int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
   if (w->N == 0 || w->N >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "qmv_argmax: need 0 < N < 2^31");
   qmm::MatArgs a = make_args(x, p, w, y);
   a.argmax_keys = (unsigned long long*)workspace;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = qmm::launch_argmax_init(a.argmax_keys, p.rows, s);
-  if (e == hipSuccess) e = qmm::launch_decode(a, s);
-  if (e == hipSuccess) e = qmm::launch_argmax_finish(a.argmax_keys, p.rows, out_index, out_value, s);
-  return launch_status(e);
+  a.argmax_count = (unsigned int*)(a.argmax_keys + p.rows);
+  a.argmax_index = out_index;
+  a.argmax_value = out_value;
+  return launch_status(qmm::launch_decode(a, (hipStream_t)stream));
 }
 
 // Shared validation of the whole-row dequantization entry points.

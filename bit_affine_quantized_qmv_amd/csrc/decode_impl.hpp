@@ -451,6 +451,41 @@ __device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int mask
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Merge a workgroup's key for one row into the global key.  The atomic returns the old key
+// and the value is consumed, so the thread waits until the merge has been performed at the
+// device-wide point where every workgroup's atomics on the key are ordered.
+__device__ inline void argmax_publish(unsigned long long* key, unsigned long long v) {
+  const unsigned long long old = __hip_atomic_fetch_max(key, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::"v"(old));
+}
+
+// Completion of the fused argmax inside the decode kernel.  Every workgroup, once all its
+// threads have published their row keys (argmax_publish), counts itself done; the last one to
+// count turns each row's key into (index, value) and sets the keys and the counter back to
+// zero, so the workspace is all-zero again when the kernel ends.  Every access to the keys and
+// the counter is a device-scope atomic, so no cache write-back is needed: a key merge is
+// performed before its workgroup counts itself, and the last workgroup reads the keys after
+// its count has returned.  `last` is a workgroup-shared word that is free once every thread
+// has arrived here (it is first written after the barrier below).  Called by every thread.
+__device__ inline void argmax_complete(const MatArgs& a, int64_t total_rows, unsigned* last) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned wgs = gridDim.x * gridDim.y * gridDim.z;
+    const unsigned done = __hip_atomic_fetch_add(a.argmax_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = done + 1 == wgs ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*last == 0u) return;
+  for (int64_t i = threadIdx.x; i < total_rows; i += blockDim.x) {
+    const unsigned long long k =
+        __hip_atomic_exchange(&a.argmax_keys[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ord = (uint32_t)(k >> 32);
+    a.argmax_index[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    if (a.argmax_value) a.argmax_value[i] = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+  }
+  if (threadIdx.x == 0) __hip_atomic_exchange(a.argmax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Reduce the wave's keys over the 16 columns of each lane group and merge them into the
 // workgroup's LDS keys `kl` (MROWS entries).
 template <int MT>

@@ -286,7 +286,8 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   if (do_argmax) {
     argmax_merge_wave<MT>(best, kl, lg, col);
     lds_barrier();
-    if (tid < rows) atomicMax(&a.argmax_keys[z * rows + tid], kl[tid]);
+    if (tid < rows) argmax_publish(&a.argmax_keys[z * rows + tid], kl[tid]);
+    argmax_complete(a, a.batches * rows, (unsigned*)kl);   // kl is free again after the barrier inside
   }
 }
 
@@ -392,7 +393,8 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     lds_barrier();
     argmax_merge_wave<MT>(best, kl, lg, col);
     lds_barrier();
-    if (tid < rows) atomicMax(&a.argmax_keys[z * rows + tid], kl[tid]);
+    if (tid < rows) argmax_publish(&a.argmax_keys[z * rows + tid], kl[tid]);
+    argmax_complete(a, a.batches * rows, (unsigned*)kl);   // kl is free again after the barrier inside
   }
 }
 

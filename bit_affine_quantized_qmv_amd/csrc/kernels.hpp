@@ -36,10 +36,15 @@ struct MatArgs {
   int64_t num_experts = 0;
   int64_t w_expert_stride = 0;
   int64_t sb_expert_stride = 0;
-  // Fused per-row argmax (decode family): when set, argmax_keys[z*rows_per_batch + m] (zeroed
-  // before the launch) receives the atomic maximum of argmax_key(y[m, n], n) over the row;
-  // y itself is then optional (nullptr: no logits are stored).
+  // Fused per-row argmax (decode family): when set, argmax_keys[z*rows_per_batch + m] (zero
+  // when the kernel starts) receives the atomic maximum of argmax_key(y[m, n], n) over the
+  // row; y itself is then optional (nullptr: no logits are stored).  The last workgroup to
+  // finish (counted in *argmax_count, zero when the kernel starts) writes argmax_index[m]
+  // and, when set, argmax_value[m], and returns the keys and the counter to zero.
   unsigned long long* argmax_keys = nullptr;
+  unsigned int* argmax_count = nullptr;
+  int32_t* argmax_index = nullptr;
+  float* argmax_value = nullptr;
 };
 
 struct QuantArgs {
@@ -78,10 +83,6 @@ struct DequantArgs {
 hipError_t launch_decode(const MatArgs& a, hipStream_t stream);
 // MFMA prefill: any rows_per_batch.
 hipError_t launch_prefill(const MatArgs& a, hipStream_t stream);
-// Fused argmax helpers: zero the keys, then turn them into (index, value).
-hipError_t launch_argmax_init(unsigned long long* keys, int64_t count, hipStream_t stream);
-hipError_t launch_argmax_finish(const unsigned long long* keys, int64_t count, int32_t* index, float* value,
-                                hipStream_t stream);
 // Standalone dequantize / embedding gather.
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 // Min/max group quantizer.

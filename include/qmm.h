@@ -178,10 +178,15 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
  *   (as float32; NaN counts as larger than any number).
  * The comparison uses the values y holds (rounded to dtype), so out_index equals an argmax
  * over the returned logits.  y may be NULL: the logits are then not written at all.
- * workspace: DEVICE, 8-byte aligned, 8 bytes per activation row (overwritten).  out_value may
- * be NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows), but K must be a
+ * workspace: DEVICE, 8-byte aligned, 8 * (rows + 1) bytes (QMM_ARGMAX_WORKSPACE_BYTES), ALL
+ * ZERO when the call's kernel starts: zero-fill it once when it is allocated.  The kernel
+ * leaves it all-zero again when it ends (its last workgroup reads the per-row keys out and
+ * clears them), so one workspace serves any number of calls in stream order; calls that may
+ * run at the same time (different streams) need workspaces of their own.  out_value may be
+ * NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows), but K must be a
  * multiple of 128 and w_row_stride of 4 words (QMM_ERR_ALIGN otherwise); 0 < N < 2^31.
- * Three kernels are enqueued: key initialisation, the decode kernel, key read-out. */
+ * One kernel is enqueued. */
+#define QMM_ARGMAX_WORKSPACE_BYTES(rows) (8 * ((rows) + 1))
 int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                        const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
                        void* stream);

@@ -199,3 +199,46 @@ def test_qmv_argmax_chunked_activations():
     assert_close(y, ref, "chunked qmv")
     ok = O.argmax_acceptable(ref["y_ref"], ref["tol"])
     assert all(int(idx[r]) in ok[r] for r in range(20))
+
+
+def test_qmv_argmax_workspace_reuse_and_graph_replay():
+    """One zero-filled workspace serves calls of different row counts (stream and chunked
+    kernels) and is all-zero after each; a captured call replays to the eager result."""
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    ws = q.argmax_workspace(32, dev)
+    for k, n in ((1024, 3001), (4096, 1500)):
+        qw = q.quantize(synth.normal_weight(n, k, 0.02, seed=1300 + k).to(dev), 128, 4, "bf16")
+        for m in (32, 5, 17, 1, 32):
+            x = synth.normal_x((m, k), "bf16", seed=1301 + m).to(dev)
+            idx, val, y = q.qmv_argmax(x, qw, workspace=ws)
+            fresh = q.qmv_argmax(x, qw)
+            torch.cuda.synchronize()
+            assert not ws.any(), (k, m)
+            assert torch.equal(idx, fresh[0]) and torch.equal(val, fresh[1]), (k, m)
+            assert torch.equal(idx, torch.argmax(y.float(), dim=1).to(torch.int32)), (k, m)
+    qw = q.quantize(synth.normal_weight(3001, 1024, 0.02, seed=1310).to(dev), 64, 4, "bf16")
+    x = synth.normal_x((32, 1024), "bf16", seed=1311).to(dev)
+    idx = torch.empty(32, dtype=torch.int32, device=dev)
+    val = torch.empty(32, dtype=torch.float32, device=dev)
+    y = torch.empty(32, 3001, dtype=torch.bfloat16, device=dev)
+    eager = q.qmv_argmax(x, qw, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q.qmv_argmax(x, qw, workspace=ws, out=y, out_index=idx, out_value=val)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qmv_argmax(x, qw, workspace=ws, out=y, out_index=idx, out_value=val)
+    for rep in range(4):
+        idx.fill_(-1)
+        val.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, eager[0]) and torch.equal(val, eager[1]) and torch.equal(y, eager[2]), rep
+        assert not ws.any(), rep
+        x2 = synth.normal_x((32, 1024), "bf16", seed=rep).to(dev)      # eager work between replays
+        q.qmv_argmax(x2, qw, workspace=ws)
+        torch.cuda.synchronize()
