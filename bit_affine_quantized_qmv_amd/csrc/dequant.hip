@@ -5,8 +5,10 @@
 // packed weight back to a dense tensor) and src(r) = index[r] for the row gather of a
 // quantized embedding table (Metal Kernel Bits=8 final report, section 3.2: dequantizing
 // single rows).  A gather index outside [0, N) gives a NaN row.  One thread handles one
-// 32-code run: it loads BITS code words, the run's scale and bias, and stores 64 bytes.
+// 8-code chunk (16 output bytes), consecutive threads consecutive chunks of a row, so each
+// wave's store covers 1 KB of contiguous output.
 #include <algorithm>
+#include <climits>
 
 #include "dequant_impl.hpp"
 #include "kernels.hpp"
@@ -16,38 +18,43 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <class T, int BITS>
-__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(const DequantArgs a) {
-  const uint32_t units_per_row = (uint32_t)(a.K / 32);
-  const int64_t total = a.rows * (int64_t)units_per_row;
-  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = u / units_per_row;
-    const int j = (int)(u - r * units_per_row);
-    int64_t src = a.index ? (int64_t)a.index[r] : r;
+template <class T, int BITS, class I>
+__device__ inline void dequant_chunks(const DequantArgs& a, I total, I chunks_per_row) {
+  const int gs_shift = __builtin_ctz((unsigned)a.group_size);   // group sizes are powers of two
+  for (I c = (I)blockIdx.x * kThreads + threadIdx.x; c < total; c += (I)gridDim.x * kThreads) {
+    const I r = c / chunks_per_row;
+    const I kc = c - r * chunks_per_row;
+    int64_t src = a.index ? (int64_t)a.index[r] : (int64_t)r;
     const bool bad = src < 0 || src >= a.N;
     src = bad ? 0 : src;
-    uint32_t w[BITS];
-    load_codes<BITS>(w, a.w + src * a.w_row_stride + (int64_t)j * BITS);
-    const int g = (32 * j) / a.group_size;
-    const uint16_t* sp = (const uint16_t*)a.scales + src * a.sb_row_stride + g;
-    const uint16_t* bp = (const uint16_t*)a.biases + src * a.sb_row_stride + g;
-    u32x4 v[4];
-    dequant32<T, BITS>(w, T::to_f32(*sp), T::to_f32(*bp), v);
+    const int64_t k0 = 8 * (int64_t)kc;
+    const int64_t g = k0 >> gs_shift;
+    const float s = T::to_f32(((const uint16_t*)a.scales)[src * a.sb_row_stride + g]);
+    const float b = T::to_f32(((const uint16_t*)a.biases)[src * a.sb_row_stride + g]);
+    u32x4 v = dequant8<T, BITS>(a.w + src * a.w_row_stride, k0, s, b);
     if (bad) {
       const uint32_t nan2 = T::kDtype == 1 ? 0x7FC07FC0u : 0x7E007E00u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = u32x4{nan2, nan2, nan2, nan2};
+      v = u32x4{nan2, nan2, nan2, nan2};
     }
-    u32x4* dst = (u32x4*)((uint16_t*)a.out + r * a.out_row_stride + 32 * j);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) dst[c] = v[c];
+    *(u32x4*)((uint16_t*)a.out + (int64_t)r * a.out_row_stride + k0) = v;
   }
 }
 
 template <class T, int BITS>
+__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(const DequantArgs a) {
+  const int64_t cpr = a.K / 8;
+  const int64_t total = a.rows * cpr;
+  // 32-bit index arithmetic whenever the chunk count fits
+  if (total <= (int64_t)UINT_MAX - (int64_t)gridDim.x * kThreads)
+    dequant_chunks<T, BITS, uint32_t>(a, (uint32_t)total, (uint32_t)cpr);
+  else
+    dequant_chunks<T, BITS, uint64_t>(a, (uint64_t)total, (uint64_t)cpr);
+}
+
+template <class T, int BITS>
 hipError_t launch_bits(const DequantArgs& a, hipStream_t stream) {
-  const int64_t total = a.rows * (a.K / 32);
-  const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 256 * 16);
+  const int64_t total = a.rows * (a.K / 8);
+  const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 256 * 32);
   hipLaunchKernelGGL((dequant_rows_kernel<T, BITS>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -67,4 +67,27 @@ __device__ inline void dequant32(const uint32_t (&w)[BITS], float s, float b, u3
   }
 }
 
+// Eight codes starting at code k0 of a row (any k0 that is a multiple of 8) -> one 8-value
+// output chunk, w~ = RNE_dtype(fma(s, q, b)) as in dequant32.  The codes occupy 8*BITS bits
+// from bit k0*BITS of the row's word stream; the second word is read only when they reach
+// into it (so nothing past the row's last code is touched).
+template <class T, int BITS>
+__device__ inline u32x4 dequant8(const uint32_t* row, int64_t k0, float s, float b) {
+  const int64_t bit0 = k0 * BITS;
+  const uint32_t* p = row + (bit0 >> 5);
+  const int sh = (int)(bit0 & 31);
+  const uint32_t lo = p[0];
+  const uint32_t hi = sh + 8 * BITS > 32 ? p[1] : 0u;
+  const uint64_t v = ((((uint64_t)hi) << 32) | lo) >> sh;
+  float q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = (float)((uint32_t)(v >> (e * BITS)) & ((1u << BITS) - 1u));
+  u32x4 out;
+  out.x = T::pack2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
+  out.y = T::pack2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
+  out.z = T::pack2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
+  out.w = T::pack2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
+  return out;
+}
+
 }  // namespace qmm
