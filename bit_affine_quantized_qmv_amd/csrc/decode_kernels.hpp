@@ -29,6 +29,10 @@ constexpr int kChunkXBytes = 64 * 1024;
 constexpr int kStreamWaves = QMM_STREAM_WAVES;
 constexpr int kStreamThreads = 64 * kStreamWaves;
 constexpr int kPair = 2;   // weight tiles consumed together per slot
+#ifndef QMM_RING_FACTOR
+#define QMM_RING_FACTOR 2
+#endif
+constexpr int kRingFactor = QMM_RING_FACTOR;   // sub-blocks of weight loads in flight
 #ifndef QMM_Y_LDS
 #define QMM_Y_LDS 0
 #endif
@@ -36,17 +40,18 @@ constexpr bool kYLds = QMM_Y_LDS != 0;   // full tile pairs stored through LDS
 
 template <class T, int BITS, int GS, int MT, int D, bool SBB>
 __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_kernel(const MatArgs a,
-                                                                                     const int tiles_base,
-                                                                                     const int tiles_rem) {
+                                                                                     const int pairs_base,
+                                                                                     const int pairs_rem) {
   // The slots of a wave's tile pairs form one stream, consumed in sub-blocks of D slots (D
   // divides the slots per tile, so a pair always ends on a sub-block boundary).  Weight
-  // loads run 2*D slots ahead of consumption (a ring of 2*D slots); with SBB the scales and
+  // loads run kRingFactor*D slots ahead of consumption (a ring of that many slots); with SBB the scales and
   // biases are loaded once per sub-block, one vector load per tile row, D slots ahead, into
   // two register sets used by alternate sub-blocks; without it each slot carries its own.
   using S = Slot<BITS, GS>;
   constexpr int MROWS = 16 * MT;
   constexpr int TN = kPair;
-  constexpr int R = 2 * D;
+  constexpr int RF = kRingFactor;
+  constexpr int R = RF * D;
   constexpr bool kBuf = BITS == 4 || BITS == 8;
   static_assert(!SBB || kBuf, "block scale/bias loads use the buffer path");
   constexpr int NHB = D * S::kGroups;   // scale (or bias) halfwords per tile row per sub-block
@@ -77,14 +82,18 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     sb_voff[t] = (16 * t + col) * sb_row_bytes;
   }
 
-  // Balanced split of the 16-row tiles over the grid's waves: tiles_rem waves take
-  // tiles_base + 1 tiles, the others tiles_base (both computed on the host).  Ranges are
-  // assigned in the order (wave-in-workgroup, workgroup), so the waves holding an extra tile
-  // are spread over all workgroups (and CUs).  A wave walks its range two tiles at a time;
-  // when the range is odd, the last pair's second tile is empty (zero loads, no store).
+  // Balanced split of the tile pairs (16-row tiles taken two at a time) over the grid's
+  // waves: pairs_rem waves take pairs_base + 1 pairs, the others pairs_base (both computed on
+  // the host).  Ranges are assigned in the order (wave-in-workgroup, workgroup), so the waves
+  // holding an extra pair are spread over all workgroups and, within a workgroup, over
+  // different SIMDs first.  Only the very last pair of the matrix can have an empty second
+  // tile (zero loads, no store).
   const int v = wave * (int)gridDim.x + (int)blockIdx.x;
-  const int64_t t_begin = (int64_t)v * tiles_base + min(v, tiles_rem);
-  const int64_t t_end = t_begin + tiles_base + (v < tiles_rem ? 1 : 0);
+  const int64_t n_tiles = (a.N + 15) >> 4;
+  const int64_t p_begin = (int64_t)v * pairs_base + min(v, pairs_rem);
+  const int64_t p_end = p_begin + pairs_base + (v < pairs_rem ? 1 : 0);
+  const int64_t t_begin = p_begin * TN;
+  const int64_t t_end = p_end * TN < n_tiles ? p_end * TN : n_tiles;
   const int nit = K / S::kSpan;              // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
   uint16_t* ys = (uint16_t*)(sxs + (K / GS + kSxPad) * MROWS) + wave * MROWS * kYRow;
@@ -184,25 +193,45 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   // come first and the weight prefetch after them.
   const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
   const int nbatch = stage_batches<MROWS>(K, kStreamThreads);
-  for (int batch = 0; batch < nbatch; ++batch) {
+  auto prefetch = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SBB) issue_sb(scA, biA);
+#pragma unroll
+    for (int rr = 0; rr < RF; ++rr) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) issue_w(j, rr * D + j);
+      w_next();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#ifndef QMM_EARLY_W
+#define QMM_EARLY_W 0
+#endif
+  if (QMM_EARLY_W && nbatch == 1) {
+    // activation loads first, the weight prefetch right behind them (loads return in issue
+    // order, so waiting for the activations does not wait for the weights)
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads);
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads);
+    prefetch();
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
+    zero_sx_pad<MT>(sxs, K / GS, tid);
+    if (do_argmax && tid < MROWS) kl[tid] = 0ull;
+    lds_barrier();
+    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
+    lds_barrier();
+  } else {
+    for (int batch = 0; batch < nbatch; ++batch) {
+      XStage<MROWS> st;
+      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads);
+      stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
+    }
+    zero_sx_pad<MT>(sxs, K / GS, tid);
+    if (do_argmax && tid < MROWS) kl[tid] = 0ull;
+    lds_barrier();
+    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
+    lds_barrier();
+    prefetch();
   }
-  zero_sx_pad<MT>(sxs, K / GS, tid);
-  if (do_argmax && tid < MROWS) kl[tid] = 0ull;
-  lds_barrier();
-  sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (SBB) issue_sb(scA, biA);
-#pragma unroll
-  for (int j = 0; j < D; ++j) issue_w(j, j);
-  w_next();
-#pragma unroll
-  for (int j = 0; j < D; ++j) issue_w(j, D + j);
-  w_next();
-  __builtin_amdgcn_sched_barrier(0);
   // (waves without tiles still take part in the argmax barrier below)
   if (t_end <= t_begin && !do_argmax) return;
 
@@ -223,7 +252,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
 
   // ---- consumption: sub-block = D slots of ring half `rbase`, scale/bias set (sc, bi);
   // the next sub-block's scales/biases go to the other set, each consumed slot is refilled
-  // right away with the slot 2*D ahead (the scheduling barriers keep the refills there)
+  // right away with the slot R ahead (the scheduling barriers keep the refills there)
   int64_t c_p = t_begin;
   int c_kb = 0;
   auto sub_block = [&](int rbase, const SbRegs<NHB>(&sc)[TN], const SbRegs<NHB>(&bi)[TN],
@@ -279,9 +308,19 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     }
   };
   const int64_t nsub = (t_end - t_begin + TN - 1) / TN * (nit / D);
-  for (int64_t i = 0; i < nsub; i += 2) {
-    sub_block(0, scA, biA, scB, biB);
-    if (i + 1 < nsub) sub_block(D, scB, biB, scA, biA);
+  // one loop trip walks the ring once (twice when RF is odd, so the scale/bias sets, which
+  // alternate per sub-block, line up again)
+  constexpr int UB = RF % 2 == 0 ? RF : 2 * RF;
+  for (int64_t i = 0; i < nsub; i += UB) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (u == 0 || i + u < nsub) {
+        if (u % 2 == 0)
+          sub_block((u % RF) * D, scA, biA, scB, biB);
+        else
+          sub_block((u % RF) * D, scB, biB, scA, biA);
+      }
+    }
   }
   if (do_argmax) {
     argmax_merge_wave<MT>(best, kl, lg, col);
@@ -415,17 +454,17 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
     per_cu = nb > 0 ? nb : 1;
     lds_cached = lds;
   }
-  // one full wave of workgroups (every CU at its occupancy), tiles spread over all waves
-  const int64_t n_tiles = (a.N + 15) / 16;
+  // one full wave of workgroups (every CU at its occupancy), tile pairs spread over all waves
+  const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
 #ifndef QMM_MAX_WG_PER_CU
 #define QMM_MAX_WG_PER_CU 8
 #endif
   const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
-  const int64_t blocks = std::min<int64_t>(full, (n_tiles + kStreamWaves - 1) / kStreamWaves);
+  const int64_t blocks = std::min<int64_t>(full, (n_pairs + kStreamWaves - 1) / kStreamWaves);
   const int64_t waves_total = blocks * kStreamWaves;
-  if (n_tiles / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (n_pairs / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a,
-                     (int)(n_tiles / waves_total), (int)(n_tiles % waves_total));
+                     (int)(n_pairs / waves_total), (int)(n_pairs % waves_total));
   return hipGetLastError();
 }
 
@@ -451,7 +490,7 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
 #endif
   if (QMM_MAX_BLOCK_SLOTS >= 8 && nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
   if (QMM_MAX_BLOCK_SLOTS >= 4 && nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
-  if (nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
+  if (QMM_MAX_BLOCK_SLOTS >= 2 && nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
   return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
 }
 
