@@ -86,7 +86,9 @@ struct SbRegs {
     } else if constexpr (KG == 2) {   // base is even
       return lg < 2 ? (v[base >> 1] >> (16 * lg)) & 0xFFFFu : 0u;
     } else {                          // KG == 4, base a multiple of 4
-      const uint32_t w = (lg & 2) ? v[(base >> 1) + 1] : v[base >> 1];
+      // an arithmetic select: a conditional one can become a dynamically indexed (scratch) array
+      const uint32_t lo = v[base >> 1], hi = v[(base >> 1) + 1];
+      const uint32_t w = lo ^ ((lo ^ hi) & (0u - (uint32_t)((lg >> 1) & 1)));
       return (w >> (16 * (lg & 1))) & 0xFFFFu;
     }
   }
@@ -347,7 +349,46 @@ __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, i
 // staged activation chunk.
 // Scales and biases come from `sc` / `bi` (NH halfwords per tile), the slot's groups
 // starting at halfword `hbase`.
-template <class T, int BITS, int GS, int MT, int TN, int NH>
+// Bias terms of up to four consecutive groups starting at group g0, one fp32 MFMA per
+// (tile, 16-row block): A[m][k] = sum x of row m in group g0 + k, B[k][n] = b[n][g0 + k], with
+// bh[t] the bias halfword lane group lg feeds for tile t (zero on the k lanes past the groups
+// covered; their A values are the next groups' sums or the zero padding, finite either way).
+template <class T, int MT, int TN>
+__device__ inline void bias_mfma(const uint32_t (&bh)[TN], const float* sxs, int g0, f32x4 (&acc)[TN][MT], int lg,
+                                 int col) {
+  constexpr int MROWS = 16 * MT;
+  float sxa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) sxa[mt] = sxs[(g0 + lg) * MROWS + mt * 16 + col];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const float bv = T::to_f32(bh[t]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[mt], bv, acc[t][mt], 0, 0, 0);
+  }
+}
+
+// The bias halfword lane group lg feeds when one bias MFMA covers two consecutive slots of
+// KG groups each (2*KG <= 4): the first slot's groups on lanes 0..KG-1, the second's next.
+template <int KG>
+__device__ inline uint32_t pair_lane_half(const SbRegs<KG>& first, const SbRegs<KG>& second, int lg) {
+  const int h = lg < KG ? lg : lg - KG;
+  const uint32_t v = lg < KG ? first.get(h & (KG - 1)) : second.get(h & (KG - 1));
+  return lg < 2 * KG ? v : 0u;
+}
+
+// Slots per bias MFMA, the same in every decode kernel so that they agree bit for bit: two
+// when the groups are 64 or 128 codes (two or one per 128-code slot) and the slots per
+// row are even, else one.
+#ifndef QMM_MAX_BLOCK_SLOTS
+#define QMM_MAX_BLOCK_SLOTS 2
+#endif
+template <int GS>
+__device__ inline int bias_span(int slots_per_row) {
+  return (QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
+}
+
+template <class T, int BITS, int GS, int MT, int TN, int NH, bool BIAS = true>
 __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbRegs<NH> (&sc)[TN],
                                     const SbRegs<NH> (&bi)[TN], int hbase, const u32x4* xs, const float* sxs,
                                     int k_local, f32x4 (&acc)[TN][MT], f32x4 (&part)[TN][MT], int lg, int col,
@@ -383,18 +424,11 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
       }
     }
   }
-  // bias terms: A[m][k] = sum x of row m in group g0 + k, B[k][n] = b[n][g0 + k]; the k lanes
-  // past the slot's groups carry b = 0 (their A values are the next groups' sums or the zero
-  // padding, finite either way)
-  const int g0 = k_local / GS;
-  float sxa[MT];
+  if constexpr (BIAS) {
+    uint32_t bh[TN];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) sxa[mt] = sxs[(g0 + lg) * MROWS + mt * 16 + col];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const float bv = T::to_f32(bi[t].template lane_half<S::kGroups>(hbase, lg));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[mt], bv, acc[t][mt], 0, 0, 0);
+    for (int t = 0; t < TN; ++t) bh[t] = bi[t].template lane_half<S::kGroups>(hbase, lg);
+    bias_mfma<T, MT, TN>(bh, sxs, k_local / GS, acc, lg, col);
   }
 }
 

@@ -52,6 +52,9 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   constexpr int TN = kPair;
   constexpr int RF = kRingFactor;
   constexpr int R = RF * D;
+  // one bias MFMA per two slots (the launcher picks D >= 2 exactly when the slots per row
+  // are even, which is when bias_span gives 2)
+  constexpr bool kPairBias = QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && D >= 2;
   constexpr bool kBuf = BITS == 4 || BITS == 8;
   static_assert(!SBB || kBuf, "block scale/bias loads use the buffer path");
   constexpr int NHB = D * S::kGroups;   // scale (or bias) halfwords per tile row per sub-block
@@ -258,11 +261,18 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   auto sub_block = [&](int rbase, const SbRegs<NHB>(&sc)[TN], const SbRegs<NHB>(&bi)[TN],
                        SbRegs<NHB>(&sc_next)[TN], SbRegs<NHB>(&bi_next)[TN]) {
     if constexpr (SBB) issue_sb(sc_next, bi_next);
+    SbRegs<S::kGroups> b_first[TN];   // bias halfwords of the first slot of a bias pair
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       if constexpr (SBB) {
-        consume_slot<T, BITS, GS, MT, TN, NHB>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
-                                               (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+        consume_slot<T, BITS, GS, MT, TN, NHB, !kPairBias>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
+                                                           (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+        if (kPairBias && j % 2 == 1) {
+          uint32_t bh[TN];
+#pragma unroll
+          for (int t = 0; t < TN; ++t) bh[t] = bi[t].template lane_half<2 * S::kGroups>((j - 1) * S::kGroups, lg);
+          bias_mfma<T, MT, TN>(bh, sxs, (c_kb + j - 1) * S::kSpan / GS, acc, lg, col);
+        }
       } else {
         SbRegs<S::kGroups> s1[TN], b1[TN];
 #pragma unroll
@@ -270,8 +280,18 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
           s1[t] = ring[rbase + j][t].s;
           b1[t] = ring[rbase + j][t].b;
         }
-        consume_slot<T, BITS, GS, MT, TN, S::kGroups>(ring[rbase + j], s1, b1, 0, xs, sxs, (c_kb + j) * S::kSpan,
-                                                      acc, part, lg, col, gshift);
+        consume_slot<T, BITS, GS, MT, TN, S::kGroups, !kPairBias>(ring[rbase + j], s1, b1, 0, xs, sxs,
+                                                                  (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+        if (kPairBias && j % 2 == 0) {
+#pragma unroll
+          for (int t = 0; t < TN; ++t) b_first[t] = b1[t];
+        }
+        if (kPairBias && j % 2 == 1) {
+          uint32_t bh[TN];
+#pragma unroll
+          for (int t = 0; t < TN; ++t) bh[t] = pair_lane_half<S::kGroups>(b_first[t], b1[t], lg);
+          bias_mfma<T, MT, TN>(bh, sxs, (c_kb + j - 1) * S::kSpan / GS, acc, lg, col);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       issue_w(j, rbase + j);
@@ -383,6 +403,8 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     }
 
   const int nit_total = K / S::kSpan;
+  const bool pair_bias = bias_span<GS>(nit_total) == 2;
+  SbRegs<S::kGroups> b_first[TN];   // bias halfwords of the first slot of a bias pair
   SlotData<BITS, GS> cur[TN], nxt[TN];
   issue(cur, 0);
   for (int kc0 = 0; kc0 < K; kc0 += KC) {
@@ -405,8 +427,23 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
           sc[t] = cur[t].s;
           bi[t] = cur[t].b;
         }
-        consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg, col,
-                                                      gshift);
+        if (!pair_bias) {
+          consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg, col,
+                                                        gshift);
+        } else {
+          consume_slot<T, BITS, GS, MT, TN, S::kGroups, false>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg,
+                                                               col, gshift);
+          if (kit % 2 == 0) {
+#pragma unroll
+            for (int t = 0; t < TN; ++t) b_first[t] = bi[t];
+          } else {
+            // chunks hold a whole number of slot pairs, so the pair's first slot is in this chunk
+            uint32_t bh[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) bh[t] = pair_lane_half<S::kGroups>(b_first[t], bi[t], lg);
+            bias_mfma<T, MT, TN>(bh, sxs, (i - 1) * S::kSpan / GS, acc, lg, col);
+          }
+        }
       }
 #pragma unroll
       for (int t = 0; t < TN; ++t) cur[t] = nxt[t];
@@ -488,9 +525,12 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
 #ifndef QMM_MAX_BLOCK_SLOTS
 #define QMM_MAX_BLOCK_SLOTS 2
 #endif
-  if (QMM_MAX_BLOCK_SLOTS >= 8 && nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
-  if (QMM_MAX_BLOCK_SLOTS >= 4 && nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
-  if (QMM_MAX_BLOCK_SLOTS >= 2 && nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
+  if constexpr (QMM_MAX_BLOCK_SLOTS >= 8)
+    if (nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
+  if constexpr (QMM_MAX_BLOCK_SLOTS >= 4)
+    if (nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
+  if constexpr (QMM_MAX_BLOCK_SLOTS >= 2)
+    if (nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
   return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
 }
 
