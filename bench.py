@@ -30,7 +30,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 QMV_SOURCES = ["decode.cpp", "decode_b4.hip", "decode_impl.hpp", "decode_kernels.hpp",
                "device_common.hpp", "kernels.hpp"]
-QMM_T_SOURCES = ["prefill.hip", "device_common.hpp", "kernels.hpp"]
+QMM_T_SOURCES = ["prefill.hip", "dequant_impl.hpp", "device_common.hpp", "kernels.hpp"]
 
 
 def _source_hash(names):

@@ -28,7 +28,10 @@ constexpr int kChunkXBytes = 64 * 1024;
 #endif
 constexpr int kStreamWaves = QMM_STREAM_WAVES;
 constexpr int kStreamThreads = 64 * kStreamWaves;
-constexpr int kPair = 2;   // weight tiles consumed together per slot
+#ifndef QMM_PAIR
+#define QMM_PAIR 2
+#endif
+constexpr int kPair = QMM_PAIR;   // weight tiles consumed together per slot
 #ifndef QMM_RING_FACTOR
 #define QMM_RING_FACTOR 2
 #endif
@@ -311,10 +314,14 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
           argmax_update<T, MT>(best, acc[t], n, c_p + t < t_end && n < N);
         }
       }
-      if (!store_y) {
-      } else if (kYLds && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
-        store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
-      } else {
+      bool stored = !store_y;
+      if constexpr (kYLds && TN == 2) {
+        if (!stored && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
+          store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
+          stored = true;
+        }
+      }
+      if (!stored) {
 #pragma unroll
         for (int t = 0; t < TN; ++t)
           if (c_p + t < t_end) store_tile<T, MT>(acc[t], yb, rows, (c_p + t) * 16 + col, N, lg);
