@@ -194,9 +194,12 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     }
   };
 
-  // ---- prologue.  A wave that is queueing loads behind the chip-wide weight prefetch
-  // blocks every barrier it has not reached yet, so the activation staging and its barriers
-  // come first and the weight prefetch after them.
+  // ---- prologue.  When the activations are staged in one batch, every wave issues its
+  // activation loads, the workgroup meets at a barrier, and only then is the weight prefetch
+  // issued: the weights are in flight during the staging and the Σx pass, and the activation
+  // loads, ahead of them in the queue, are not delayed by them.  (A wave still issuing
+  // weight loads would hold up any barrier it has not reached, so none comes between the
+  // prefetch and the staging waits.)  Larger activations are staged batch by batch first.
   const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
   const int nbatch = stage_batches<MROWS>(K, kStreamThreads);
   auto prefetch = [&]() {
@@ -211,13 +214,15 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     __builtin_amdgcn_sched_barrier(0);
   };
 #ifndef QMM_EARLY_W
-#define QMM_EARLY_W 0
+#define QMM_EARLY_W 2
 #endif
   if (QMM_EARLY_W && nbatch == 1) {
     // activation loads first, the weight prefetch right behind them (loads return in issue
     // order, so waiting for the activations does not wait for the weights)
     XStage<MROWS> st;
     stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads);
+    // every wave's activation loads are issued before any weight load enters the queue
+    if (QMM_EARLY_W >= 2) lds_barrier();
     prefetch();
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
     zero_sx_pad<MT>(sxs, K / GS, tid);
