@@ -76,8 +76,8 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
   if (p.rows == 0 || w->N == 0) return finish(QMM_OK, "");
   if (p.rows_per_batch != 1)
     return finish(QMM_ERR_LAYOUT, "gather_qmv: x rows must fold into one strided level");
-  if (w->K % 128 || w->w_row_stride % 4)
-    return finish(QMM_ERR_ALIGN, "gather_qmv: needs K a multiple of 128 and w_row_stride a multiple of 4 words");
+  if (w->w_row_stride % 4)
+    return finish(QMM_ERR_ALIGN, "gather_qmv: needs w_row_stride a multiple of 4 words");
   if (num_experts < 1) return finish(QMM_ERR_SHAPE, "gather_qmv: num_experts must be >= 1");
   if (!expert_index) return finish(QMM_ERR_NULL, "gather_qmv: expert_index must be non-NULL");
   if ((uintptr_t)expert_index % 4) return finish(QMM_ERR_ALIGN, "gather_qmv: expert_index must be 4-byte aligned");
@@ -102,8 +102,8 @@ int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
   int rc = qmm::plan_matmul(x, x_desc, w, y ? y : (void*)&y_stand_in, y_desc, 0, 0, true, &p, &err);
   if (rc != QMM_OK) return finish(rc, err);
   if (p.rows == 0) return finish(QMM_OK, "");
-  if (w->K % 128 || w->w_row_stride % 4)
-    return finish(QMM_ERR_ALIGN, "qmv_argmax: needs K a multiple of 128 and w_row_stride a multiple of 4 words");
+  if (w->w_row_stride % 4)
+    return finish(QMM_ERR_ALIGN, "qmv_argmax: needs w_row_stride a multiple of 4 words");
   if (!out_index || !workspace) return finish(QMM_ERR_NULL, "qmv_argmax: out_index and workspace must be non-NULL");
   if ((uintptr_t)workspace % 8 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
     return finish(QMM_ERR_ALIGN, "qmv_argmax: workspace must be 8-byte, out_index/out_value 4-byte aligned");

@@ -27,8 +27,8 @@ int device_cus() {
 
 hipError_t launch_decode(const MatArgs& a, hipStream_t stream) {
   if (a.rows_per_batch > 32 || a.rows_per_batch <= 0 || a.batches > 65535) return hipErrorInvalidValue;
-  // slots are 128-code runs loaded in 16-byte pieces
-  if (a.K % 128 != 0 || a.w_row_stride % 4 != 0) return hipErrorInvalidValue;
+  // rows start on 16-byte boundaries; K is a multiple of the group size (>= 32)
+  if (a.K % 32 != 0 || a.w_row_stride % 4 != 0) return hipErrorInvalidValue;
   if (a.bits == 4) return decode::launch_decode_b4(a, stream);
   if (a.bits == 8) return decode::launch_decode_b8(a, stream);
   return decode::launch_decode_bn(a, stream);

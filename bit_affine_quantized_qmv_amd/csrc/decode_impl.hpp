@@ -94,6 +94,20 @@ struct SbRegs {
   }
 };
 
+// N halfwords of a row's scales or biases; with `valid` < N (the row's last slot when K is
+// not a multiple of the slot span) only the first `valid` are read, the rest are zero.
+template <int N>
+__device__ inline SbRegs<N> load_sb_part(const uint16_t* p, int valid) {
+  SbRegs<N> r;
+#pragma unroll
+  for (int i = 0; i < (N + 1) / 2; ++i) {
+    const uint32_t lo = 2 * i < valid ? p[2 * i] : 0u;
+    const uint32_t hi = 2 * i + 1 < N && 2 * i + 1 < valid ? p[2 * i + 1] : 0u;
+    r.v[i] = lo | (hi << 16);
+  }
+  return r;
+}
+
 template <int N>
 __device__ inline SbRegs<N> load_sb(const uint16_t* p) {
   SbRegs<N> r;
@@ -146,11 +160,18 @@ struct SlotData {
 // scales/biases at `srow`/`brow` (offset to the slot's first group).  `lg` = lane group.
 template <int BITS, int GS>
 __device__ inline void load_slot(SlotData<BITS, GS>& d, const uint32_t* wrow, const uint16_t* srow,
-                                 const uint16_t* brow, int lg, int generic_word, int row_words_left) {
+                                 const uint16_t* brow, int lg, int generic_word, int row_words_left,
+                                 int codes_left, bool sb_narrow) {
   using S = Slot<BITS, GS>;
   if constexpr (BITS == 4 || BITS == 8) {
+    // a lane's 16 bytes hold 32 (4-bit) or 16 (8-bit) consecutive codes; past the row's end
+    // (the last slot when K is not a multiple of the span) they are zero and nothing is read
+    constexpr int kLaneCodes = BITS == 4 ? 32 : 16;
 #pragma unroll
-    for (int v = 0; v < S::kVec; ++v) d.v[v] = *(const u32x4*)(wrow + 16 * v + 4 * lg);
+    for (int v = 0; v < S::kVec; ++v) {
+      const int c0 = (4 * v + lg) * kLaneCodes;
+      d.v[v] = c0 < codes_left ? *(const u32x4*)(wrow + 16 * v + 4 * lg) : u32x4{0u, 0u, 0u, 0u};
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < S::kSteps; ++c) {
@@ -160,18 +181,42 @@ __device__ inline void load_slot(SlotData<BITS, GS>& d, const uint32_t* wrow, co
       d.w[2 * c + 1] = wrow[min(idx + 1, row_words_left - 1)];
     }
   }
-  d.s = load_sb<S::kGroups>(srow);
-  d.b = load_sb<S::kGroups>(brow);
+  // halfword loads when the scale rows are not a whole number of the slot's groups (the
+  // vector loads would be misaligned) or the slot ends past K (neither can happen with one
+  // group per slot: the slot is then the group)
+  if (S::kGroups == 1 || (!sb_narrow && codes_left >= S::kSpan)) {
+    d.s = load_sb<S::kGroups>(srow);
+    d.b = load_sb<S::kGroups>(brow);
+  } else {
+    const int valid = codes_left / GS < S::kGroups ? codes_left / GS : S::kGroups;
+    d.s = load_sb_part<S::kGroups>(srow, valid);
+    d.b = load_sb_part<S::kGroups>(brow, valid);
+  }
 }
 
 // Buffer-descriptor variant of load_slot: `w_rs`, `s_rs`, `b_rs` describe the rows of a
 // tile pair (rows outside the range read as zero); the lane's row offset is in `w_voff` /
 // `sb_voff` (bytes), the slot's offset inside the row in `w_soff` / `sb_soff`.  With
 // WITH_SB false the scales and biases are loaded per block elsewhere.
+// With `sb_narrow` (scale rows not a whole number of the slot's groups, or a last slot that
+// ends past K) the scales and biases are read one halfword at a time: every halfword is then
+// aligned and range-checked on its own, so one past the described rows cannot zero a valid
+// neighbour in the same dword.
+template <int NH>
+__device__ inline void load_sb_buf_narrow(SbRegs<NH>& r, __amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+#pragma unroll
+  for (int i = 0; i < (NH + 1) / 2; ++i) {
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 4 * i, soff, 0);
+    const uint32_t hi = 2 * i + 1 < NH ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff + 4 * i + 2, soff, 0)
+                                       : 0u;
+    r.v[i] = lo | (hi << 16);
+  }
+}
+
 template <int BITS, int GS, bool WITH_SB>
 __device__ inline void load_slot_buf(SlotData<BITS, GS>& d, __amdgpu_buffer_rsrc_t w_rs,
                                      __amdgpu_buffer_rsrc_t s_rs, __amdgpu_buffer_rsrc_t b_rs, int w_voff,
-                                     int w_soff, int sb_voff, int sb_soff) {
+                                     int w_soff, int sb_voff, int sb_soff, bool sb_narrow = false) {
   using S = Slot<BITS, GS>;
   static_assert(BITS == 4 || BITS == 8, "buffer path is for 4- and 8-bit codes");
 #pragma unroll
@@ -180,8 +225,13 @@ __device__ inline void load_slot_buf(SlotData<BITS, GS>& d, __amdgpu_buffer_rsrc
     d.v[v] = u32x4{u[0], u[1], u[2], u[3]};
   }
   if constexpr (WITH_SB) {
-    load_sb_buf<S::kGroups>(d.s, s_rs, sb_voff, sb_soff);
-    load_sb_buf<S::kGroups>(d.b, b_rs, sb_voff, sb_soff);
+    if (sb_narrow) {
+      load_sb_buf_narrow<S::kGroups>(d.s, s_rs, sb_voff, sb_soff);
+      load_sb_buf_narrow<S::kGroups>(d.b, b_rs, sb_voff, sb_soff);
+    } else {
+      load_sb_buf<S::kGroups>(d.s, s_rs, sb_voff, sb_soff);
+      load_sb_buf<S::kGroups>(d.b, b_rs, sb_voff, sb_soff);
+    }
   }
 }
 
@@ -291,6 +341,17 @@ __device__ inline void stage_x_commit(const XStage<MROWS>& st, u32x4* xs, int ro
   }
 }
 
+// Zero the staged activations between k_len and k_pad (the last slot's k past K when K is
+// not a multiple of the slot span), so their products with whatever codes are loaded there
+// vanish.
+template <int BITS, int MROWS>
+__device__ inline void zero_x_pad(u32x4* xs, int k_len, int k_pad, int tid, int nthreads) {
+  const int per = nthreads / MROWS;
+  const int m = tid % MROWS;
+  for (int j8 = (k_len >> 3) + tid / MROWS; j8 < (k_pad >> 3); j8 += per)
+    xs[((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) * MROWS + m] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // Number of staging batches for a chunk of k_len.
 template <int MROWS>
 __device__ inline int stage_batches(int k_len, int nthreads) {
@@ -391,8 +452,8 @@ __device__ inline int bias_span(int slots_per_row) {
 template <class T, int BITS, int GS, int MT, int TN, int NH, bool BIAS = true>
 __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbRegs<NH> (&sc)[TN],
                                     const SbRegs<NH> (&bi)[TN], int hbase, const u32x4* xs, const float* sxs,
-                                    int k_local, f32x4 (&acc)[TN][MT], f32x4 (&part)[TN][MT], int lg, int col,
-                                    uint32_t generic_shift) {
+                                    int k_local, int k_valid, f32x4 (&acc)[TN][MT], f32x4 (&part)[TN][MT], int lg,
+                                    int col, uint32_t generic_shift) {
   using S = Slot<BITS, GS>;
   constexpr int MROWS = 16 * MT;
   constexpr int SPG = GS / 32;
@@ -414,9 +475,12 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
     }
     if ((c + 1) % SPG == 0) {
       const int gi = c / SPG;
+      // groups past K (the last slot when K is not a multiple of the span) scale by zero:
+      // their products are zero and their loaded scales need not be finite
+      const bool g_ok = k_local + gi * GS < k_valid;
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        const float sv = T::to_f32(sc[t].get(hbase + gi));
+        const float sv = g_ok ? T::to_f32(sc[t].get(hbase + gi)) : 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -425,9 +489,10 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
     }
   }
   if constexpr (BIAS) {
+    const bool g_ok = (k_local / GS + lg) * GS < k_valid;
     uint32_t bh[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) bh[t] = bi[t].template lane_half<S::kGroups>(hbase, lg);
+    for (int t = 0; t < TN; ++t) bh[t] = g_ok ? bi[t].template lane_half<S::kGroups>(hbase, lg) : 0u;
     bias_mfma<T, MT, TN>(bh, sxs, k_local / GS, acc, lg, col);
   }
 }

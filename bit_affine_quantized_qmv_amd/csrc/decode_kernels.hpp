@@ -63,8 +63,9 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   constexpr int NHB = D * S::kGroups;   // scale (or bias) halfwords per tile row per sub-block
   extern __shared__ u32x4 smem[];
   const int K = (int)a.K;
+  const int Kp = (K + S::kSpan - 1) / S::kSpan * S::kSpan;   // K rounded up to whole slots
   u32x4* xs = smem;
-  float* sxs = (float*)(smem + (K / 32) * 4 * MROWS);
+  float* sxs = (float*)(smem + (Kp / 32) * 4 * MROWS);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
   const int w_row_bytes = (int)(a.w_row_stride * 4);
   const int sb_row_bytes = (int)(a.sb_row_stride * 2);
+  const bool sb_narrow = sb_row_bytes % (2 * S::kGroups) != 0 || K % S::kSpan != 0;
   int w_voff[TN], sb_voff[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   const int64_t p_end = p_begin + pairs_base + (v < pairs_rem ? 1 : 0);
   const int64_t t_begin = p_begin * TN;
   const int64_t t_end = p_end * TN < n_tiles ? p_end * TN : n_tiles;
-  const int nit = K / S::kSpan;              // slots per tile (a multiple of D)
+  const int nit = Kp / S::kSpan;             // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
   uint16_t* ys = (uint16_t*)(sxs + (K / GS + kSxPad) * MROWS) + wave * MROWS * kYRow;
   // fused argmax: per-row keys of the workgroup, after the store staging area
@@ -144,14 +146,14 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     for (int t = 0; t < TN; ++t) {
       if constexpr (kBuf) {
         load_slot_buf<BITS, GS, !SBB>(ring[r][t], w_rs, ws_rs, wb_rs, w_voff[t], kit * S::kRowWordsPerSlot * 4,
-                                      sb_voff[t], kit * S::kGroups * 2);
+                                      sb_voff[t], kit * S::kGroups * 2, sb_narrow);
       } else {
         const int64_t n = w_p * 16 + 16 * t + col;
         const int64_t nl = n < N ? n : N - 1;
         load_slot<BITS, GS>(ring[r][t], wb.w + nl * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
                             wb.s + nl * a.sb_row_stride + kit * S::kGroups,
                             wb.b + nl * a.sb_row_stride + kit * S::kGroups, lg, gword,
-                            row_words - kit * S::kRowWordsPerSlot);
+                            row_words - kit * S::kRowWordsPerSlot, K - kit * S::kSpan, sb_narrow);
       }
     }
   };
@@ -225,6 +227,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     if (QMM_EARLY_W >= 2) lds_barrier();
     prefetch();
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
+    zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
     zero_sx_pad<MT>(sxs, K / GS, tid);
     if (do_argmax && tid < MROWS) kl[tid] = 0ull;
     lds_barrier();
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
       stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads);
       stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
     }
+    zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
     zero_sx_pad<MT>(sxs, K / GS, tid);
     if (do_argmax && tid < MROWS) kl[tid] = 0ull;
     lds_barrier();
@@ -274,12 +278,15 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     for (int j = 0; j < D; ++j) {
       if constexpr (SBB) {
         consume_slot<T, BITS, GS, MT, TN, NHB, !kPairBias>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
-                                                           (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+                                                           (c_kb + j) * S::kSpan, K, acc, part, lg, col, gshift);
         if (kPairBias && j % 2 == 1) {
+          const int g0 = (c_kb + j - 1) * S::kSpan / GS;
+          const bool g_ok = (g0 + lg) * GS < K;   // groups past K add nothing
           uint32_t bh[TN];
 #pragma unroll
-          for (int t = 0; t < TN; ++t) bh[t] = bi[t].template lane_half<2 * S::kGroups>((j - 1) * S::kGroups, lg);
-          bias_mfma<T, MT, TN>(bh, sxs, (c_kb + j - 1) * S::kSpan / GS, acc, lg, col);
+          for (int t = 0; t < TN; ++t)
+            bh[t] = g_ok ? bi[t].template lane_half<2 * S::kGroups>((j - 1) * S::kGroups, lg) : 0u;
+          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
         }
       } else {
         SbRegs<S::kGroups> s1[TN], b1[TN];
@@ -289,16 +296,19 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
           b1[t] = ring[rbase + j][t].b;
         }
         consume_slot<T, BITS, GS, MT, TN, S::kGroups, !kPairBias>(ring[rbase + j], s1, b1, 0, xs, sxs,
-                                                                  (c_kb + j) * S::kSpan, acc, part, lg, col, gshift);
+                                                                  (c_kb + j) * S::kSpan, K, acc, part, lg, col,
+                                                                  gshift);
         if (kPairBias && j % 2 == 0) {
 #pragma unroll
           for (int t = 0; t < TN; ++t) b_first[t] = b1[t];
         }
         if (kPairBias && j % 2 == 1) {
+          const int g0 = (c_kb + j - 1) * S::kSpan / GS;
+          const bool g_ok = (g0 + lg) * GS < K;
           uint32_t bh[TN];
 #pragma unroll
-          for (int t = 0; t < TN; ++t) bh[t] = pair_lane_half<S::kGroups>(b_first[t], b1[t], lg);
-          bias_mfma<T, MT, TN>(bh, sxs, (c_kb + j - 1) * S::kSpan / GS, acc, lg, col);
+          for (int t = 0; t < TN; ++t) bh[t] = g_ok ? pair_lane_half<S::kGroups>(b_first[t], b1[t], lg) : 0u;
+          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -382,6 +392,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   const int64_t N = a.N;
   const int K = (int)a.K;
   const int row_words = (K * BITS) >> 5;
+  const bool sb_narrow = (a.sb_row_stride * 2) % (2 * S::kGroups) != 0;
   uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
 
   int gword = 0;
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
       load_slot<BITS, GS>(d[t], wb.w + nl[t] * a.w_row_stride + (int64_t)kit * S::kRowWordsPerSlot,
                           wb.s + nl[t] * a.sb_row_stride + kit * S::kGroups,
                           wb.b + nl[t] * a.sb_row_stride + kit * S::kGroups, lg, gword,
-                          row_words - kit * S::kRowWordsPerSlot);
+                          row_words - kit * S::kRowWordsPerSlot, K - kit * S::kSpan, sb_narrow);
   };
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
       part[t][mt] = zero4;
     }
 
-  const int nit_total = K / S::kSpan;
+  const int nit_total = (K + S::kSpan - 1) / S::kSpan;   // the last slot may end past K
   const bool pair_bias = bias_span<GS>(nit_total) == 2;
   SbRegs<S::kGroups> b_first[TN];   // bias halfwords of the first slot of a bias pair
   SlotData<BITS, GS> cur[TN], nxt[TN];
@@ -422,13 +433,15 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   for (int kc0 = 0; kc0 < K; kc0 += KC) {
     const int kcl = min(KC, K - kc0);
     lds_barrier();
+    const int kclp = (kcl + S::kSpan - 1) / S::kSpan * S::kSpan;
     stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads);
+    zero_x_pad<BITS, MROWS>(xs, kcl, kclp, tid, kThreads);
     zero_sx_pad<MT>(sxs, kcl / GS, tid);
     lds_barrier();
     sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane);
     lds_barrier();
     const int kit0 = kc0 / S::kSpan;
-    const int nit = kcl / S::kSpan;
+    const int nit = kclp / S::kSpan;
     for (int i = 0; i < nit; ++i) {
       const int kit = kit0 + i;
       issue(nxt, min(kit + 1, nit_total - 1));
@@ -440,20 +453,22 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
           bi[t] = cur[t].b;
         }
         if (!pair_bias) {
-          consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg, col,
-                                                        gshift);
+          consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, kcl, acc, part, lg,
+                                                        col, gshift);
         } else {
-          consume_slot<T, BITS, GS, MT, TN, S::kGroups, false>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, acc, part, lg,
-                                                               col, gshift);
+          consume_slot<T, BITS, GS, MT, TN, S::kGroups, false>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, kcl, acc, part,
+                                                               lg, col, gshift);
           if (kit % 2 == 0) {
 #pragma unroll
             for (int t = 0; t < TN; ++t) b_first[t] = bi[t];
           } else {
             // chunks hold a whole number of slot pairs, so the pair's first slot is in this chunk
+            const int g0 = (i - 1) * S::kSpan / GS;
+            const bool g_ok = (g0 + lg) * GS < kcl;
             uint32_t bh[TN];
 #pragma unroll
-            for (int t = 0; t < TN; ++t) bh[t] = pair_lane_half<S::kGroups>(b_first[t], bi[t], lg);
-            bias_mfma<T, MT, TN>(bh, sxs, (i - 1) * S::kSpan / GS, acc, lg, col);
+            for (int t = 0; t < TN; ++t) bh[t] = g_ok ? pair_lane_half<S::kGroups>(b_first[t], bi[t], lg) : 0u;
+            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
           }
         }
       }
@@ -533,7 +548,7 @@ hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
 // Slots per main-loop block: the largest of 8, 4, 2, 1 dividing the slots per tile.
 template <class T, int BITS, int GS, int MT>
 hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
-  const int nit = (int)(a.K / Slot<BITS, GS>::kSpan);
+  const int nit = (int)((a.K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
 #ifndef QMM_MAX_BLOCK_SLOTS
 #define QMM_MAX_BLOCK_SLOTS 2
 #endif
@@ -554,9 +569,10 @@ hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int GS>
+template <int BITS, int MT, int GS>
 constexpr int stream_lds_bytes(int K) {
-  return 16 * MT * K * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0) +
+  const int Kp = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan * Slot<BITS, GS>::kSpan;
+  return 16 * MT * Kp * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0) +
          16 * MT * 8;
 }
 
@@ -564,11 +580,40 @@ template <class T, int BITS, int GS>
 hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   const int K = (int)a.K;
   if (a.rows_per_batch <= 16) {
-    const int lds = stream_lds_bytes<1, GS>(K);
+    const int lds = stream_lds_bytes<BITS, 1, GS>(K);
     return lds <= kLdsLimit ? launch_stream<T, BITS, GS, 1>(a, stream, lds) : launch_chunk<T, BITS, GS, 1>(a, stream);
   }
-  const int lds = stream_lds_bytes<2, GS>(K);
-  return lds <= kLdsLimit ? launch_stream<T, BITS, GS, 2>(a, stream, lds) : launch_chunk<T, BITS, GS, 2>(a, stream);
+  const int lds = stream_lds_bytes<BITS, 2, GS>(K);
+  if (lds <= kLdsLimit) return launch_stream<T, BITS, GS, 2>(a, stream, lds);
+  // 17..32 rows whose activations do not fit in LDS at once: when 16 activation rows do,
+  // run the one-block streaming kernel twice (rows 0..15, then the rest), which keeps every
+  // row's arithmetic that of a call of at most 16 rows.  The second pass needs the rows to
+  // continue one 16-row block further at a fixed offset: one segment, or segments that are
+  // whole 16-row blocks; one grid slice.
+  const int lds1 = stream_lds_bytes<BITS, 1, GS>(K);
+  const int64_t rows = a.rows_per_batch;
+  const bool one_seg = a.seg_rows >= rows;
+  if (lds1 <= kLdsLimit && a.batches == 1 && (one_seg || a.seg_rows % 16 == 0)) {
+    MatArgs lo = a, hi = a;
+    lo.rows_per_batch = 16;
+    hi.rows_per_batch = rows - 16;
+    const int64_t x_off = one_seg ? 16 * a.row_stride : (16 / a.seg_rows) * a.seg_stride + (16 % a.seg_rows) * a.row_stride;
+    hi.x = (const uint16_t*)a.x + x_off;
+    if (one_seg) {
+      lo.seg_rows = 16;
+      hi.seg_rows = rows - 16;
+    }
+    if (a.y) hi.y = (uint16_t*)a.y + 16 * a.N;
+    if (a.argmax_keys) {
+      hi.argmax_keys = a.argmax_keys + 16;
+      hi.argmax_index = a.argmax_index + 16;
+      if (a.argmax_value) hi.argmax_value = a.argmax_value + 16;
+    }
+    hipError_t e = launch_stream<T, BITS, GS, 1>(lo, stream, lds1);
+    if (e != hipSuccess) return e;
+    return launch_stream<T, BITS, GS, 1>(hi, stream, lds1);
+  }
+  return launch_chunk<T, BITS, GS, 2>(a, stream);
 }
 
 template <int BITS>

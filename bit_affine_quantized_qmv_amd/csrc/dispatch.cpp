@@ -112,11 +112,11 @@ int plan_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_des
   p.batches = 1;
   p.rows_per_batch = M;
   p.seg_rows = M > 0 ? M : 1;
-  // The decode kernels take K a multiple of 128 and rows that start on 16-byte boundaries;
-  // other shapes (any K that is a multiple of the group size) go through the MFMA kernel at
-  // every row count: its partial last k step is masked, and its per-row arithmetic does not
+  // The decode kernels take rows that start on 16-byte boundaries (any K that is a multiple
+  // of the group size: a last slot that ends past K is masked); weights padded to other row
+  // strides go through the MFMA kernel at every row count, whose per-row arithmetic does not
   // depend on the row count either.
-  p.family = (M <= QMM_DECODE_MAX_ROWS && K % 128 == 0 && w->w_row_stride % 4 == 0) ? 0 : 1;
+  p.family = (M <= QMM_DECODE_MAX_ROWS && w->w_row_stride % 4 == 0) ? 0 : 1;
   if (entry == 0 && M > QMM_DECODE_MAX_ROWS)
     return fail(err, QMM_ERR_SHAPE, "qmv takes at most %d activation rows, got %lld; use qmm_t",
                 QMM_DECODE_MAX_ROWS, (long long)M);

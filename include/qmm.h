@@ -132,11 +132,11 @@ int32_t qmm_quantize(const float* w, int64_t N, int64_t K, int64_t w_row_stride,
  * Alignment: x, w_packed 16-byte aligned; x strides (except the last) multiples of 8;
  * w_row_stride a multiple of the 32-code run: 4 words for 4- and 8-bit codes, 2 words for
  * 2- and 6-bit codes, 1 word otherwise.
- * Any K that is a multiple of group_size is accepted.  When K is a multiple of 128 and
- * w_row_stride a multiple of 4 words the decode kernels run; otherwise (e.g. K = 96 with
- * group_size 32, or rows padded to an odd word count) the call runs the MFMA kernel that
- * qmm_t uses for many rows, whose last k step is masked (MLX pull request 4516, second commit text: inputs that
- * are not aligned for the fast qmv kernel take the generic kernel and its guarded tail).
+ * Any K that is a multiple of group_size is accepted (e.g. K = 96 with group_size 32): the
+ * decode kernels mask a last 128-code slot that ends past K (MLX pull request 4516, second
+ * commit text: inputs that are not aligned for the fast qmv kernel need a guarded tail).
+ * When w_row_stride is not a multiple of 4 words (rows padded to an odd word count) the
+ * call runs the MFMA kernel that qmm_t uses for many rows.
  * M == 0 or N == 0 is a no-op returning QMM_OK. */
 int32_t qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
             void* y, const qmm_tensor_desc_t* y_desc, uint32_t flags, void* stream);
@@ -163,8 +163,8 @@ int32_t qmm_t(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_d
  * stack).  Each row runs the decode kernels on its own (at most 65535 rows), and its result
  * is bit-identical to qmv on that row with expert e's weight.
  * Strides: w_expert_stride >= N * w_row_stride (a multiple of 4), sb_expert_stride >=
- * N * sb_row_stride.  K must be a multiple of 128 and w_row_stride of 4 words (the decode
- * kernels' shapes; QMM_ERR_ALIGN otherwise).  Other requirements as for qmv.  Zero rows or
+ * N * sb_row_stride.  w_row_stride must be a multiple of 4 words (the decode kernels' row
+ * alignment; QMM_ERR_ALIGN otherwise).  Other requirements as for qmv.  Zero rows or
  * N == 0 is a no-op. */
 int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w,
                        int64_t num_experts, int64_t w_expert_stride, int64_t sb_expert_stride,
@@ -183,8 +183,8 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
  * leaves it all-zero again when it ends (its last workgroup reads the per-row keys out and
  * clears them), so one workspace serves any number of calls in stream order; calls that may
  * run at the same time (different streams) need workspaces of their own.  out_value may be
- * NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows), but K must be a
- * multiple of 128 and w_row_stride of 4 words (QMM_ERR_ALIGN otherwise); 0 < N < 2^31.
+ * NULL.  Contract otherwise as for qmv (at most QMM_DECODE_MAX_ROWS rows), but w_row_stride
+ * must be a multiple of 4 words (QMM_ERR_ALIGN otherwise); 0 < N < 2^31.
  * One kernel is enqueued. */
 #define QMM_ARGMAX_WORKSPACE_BYTES(rows) (8 * ((rows) + 1))
 int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,

@@ -135,18 +135,20 @@ def test_empty_is_a_plan():
     assert p["rows"] == 3
 
 
-def test_unaligned_k_and_odd_row_strides_take_the_mfma_kernel():
-    """K a multiple of the group size but not of 128, or weight rows padded to a word count
-    the decode kernels cannot load in 16-byte pieces, plan the MFMA kernel at every row count
-    (MLX pull request 4516, second commit text: unaligned inputs take the generic kernel)."""
+def test_unaligned_k_and_odd_row_strides():
+    """K a multiple of the group size but not of 128 stays on the decode kernels up to 32
+    rows (their last slot is masked); weight rows padded to a word count the decode kernels
+    cannot load in 16-byte pieces plan the MFMA kernel at every row count (MLX pull request
+    4516, second commit text: unaligned inputs take the generic kernel)."""
     for m in (1, 7, 32, 33, 500):
+        dec = 0 if m <= 32 else 1
         p = _plan([m, 1056], [1056, 1], group_size=32)
-        assert (p["rows"], p["family"]) == (m, 1)
+        assert (p["rows"], p["family"]) == (m, dec)
         p = _plan([m, 1088], [1088, 1], group_size=64, entry=0 if m <= 32 else 1)
-        assert p["family"] == 1
+        assert p["family"] == dec
         assert _plan([m, K], [K, 1], bits=3, w_row_stride=97)["family"] == 1
-        assert _plan([m, K], [K, 1], bits=3, w_row_stride=100)["family"] == (0 if m <= 32 else 1)
-    assert _plan([4, 32], [32, 1], group_size=32, entry=0)["family"] == 1
+        assert _plan([m, K], [K, 1], bits=3, w_row_stride=100)["family"] == dec
+    assert _plan([4, 32], [32, 1], group_size=32, entry=0)["family"] == 0
     # the run alignment of each code width: 4 words for 4/8-bit, 2 for 2/6-bit, 1 otherwise
     _err([3, K], [K, 1], -5, bits=4, w_row_stride=130)
     _err([3, K], [K, 1], -5, bits=8, w_row_stride=258)

@@ -238,3 +238,26 @@ def test_empty_and_errors(dev):
     assert e.value.code == -3
     with pytest.raises(q.QmmError):
         q.qmm_t(torch.zeros(4, 128, dtype=torch.float16, device=dev), qw)
+
+
+def test_large_k_seventeen_to_32_rows(dev):
+    """17..32 rows at K = 4096 (activations too large for one LDS block of 32 rows): rows
+    equal the single-row calls bit for bit, for one segment, for a two-level layout of
+    16-row segments, and with the fused argmax."""
+    import bit_affine_quantized_qmv_amd as q
+    n, k = 3000, 4096
+    qw = q.quantize(synth.normal_weight(n, k, 0.02, seed=41).to(dev), 128, 4, "bf16")
+    x = synth.normal_x((32, k), "bf16", seed=42).to(dev)
+    singles = torch.cat([q.qmv(x[i:i + 1], qw) for i in range(32)])
+    for m in (17, 20, 32):
+        assert torch.equal(q.qmv(x[:m], qw), singles[:m]), m
+    buf = synth.normal_x((2, 20, k), "bf16", seed=43).to(dev)
+    view = buf[:, :16, :]                          # two segments of 16 rows
+    y = q.qmv(view, qw)
+    for b in range(2):
+        for i in (0, 15):
+            assert torch.equal(y[b, i], q.qmv(view[b, i:i + 1], qw)[0]), (b, i)
+    assert_close(y.reshape(32, n), reference_rows(gather(buf, view), qw, "bf16"), "two segments")
+    idx, val, yl = q.qmv_argmax(x[:20], qw)
+    assert torch.equal(yl, singles[:20])
+    assert torch.equal(idx, torch.argmax(yl.float(), dim=1).to(torch.int32))

@@ -1,8 +1,8 @@
-"""GPU parity of the unaligned-K path: K a multiple of the group size but not of 128, and
-weight rows padded to word counts the decode kernels do not take.  These calls run the MFMA
-kernel with a masked last k step at every row count (MLX pull request 4516, second commit
-text: inputs that are not aligned for the fast qmv kernel take the generic kernel and its
-guarded tail)."""
+"""GPU parity of the unaligned-K path: K a multiple of the group size but not of 128 (the
+decode kernels mask a last slot that ends past K; the MFMA kernel masks its last k step),
+and weight rows padded to word counts the decode kernels do not take, which run the MFMA
+kernel at every row count (MLX pull request 4516, second commit text: inputs that are not
+aligned for the fast qmv kernel take the generic kernel and its guarded tail)."""
 import numpy as np
 import pytest
 import torch
@@ -52,21 +52,26 @@ def test_unaligned_k_parity(dev, bits, dtype):
                 assert torch.equal(q.qmv(x, qw), y), (k, m)
 
 
-def test_unaligned_rows_independent_of_row_count(dev):
-    """Row i of a 70-row call equals the single-row call on row i bit for bit, through qmv,
-    qmm_t and a strided [B, 1, K] batch."""
+@pytest.mark.parametrize("k,gs", [(1056, 32), (4128, 32), (1088, 64), (96, 32)])
+def test_unaligned_batch_invariance(dev, k, gs):
+    """Row i of every [B, 1, K] decode call (B = 1..32) equals the single-row call bit for
+    bit at unaligned K, also across the change from the streaming to the chunked decode
+    kernel (K = 4128 at B > 16), through a strided batch and the forced per-row plan."""
     import bit_affine_quantized_qmv_amd as q
-    n, k = 1000, 1056
-    for bits in (4, 3, 8):
-        qw = q.quantize(synth.normal_weight(n, k, 0.02, seed=bits).to(dev), 32, bits, "bf16")
-        x = synth.normal_x((70, k), "bf16", seed=bits).to(dev)
-        y = q.qmm_t(x, qw)
-        for i in (0, 1, 31, 32, 69):
-            assert torch.equal(q.qmv(x[i:i + 1], qw)[0], y[i]), (bits, i)
-        assert torch.equal(q.qmv(x[:32], qw), y[:32])
-        xb = x[:16].view(16, 1, k)
-        assert torch.equal(q.qmv(xb, qw).view(16, n), y[:16])
-        assert torch.equal(q.qmv(xb, qw, flags=q.QMM_FLAG_FORCE_STRIDED).view(16, n), y[:16])
+    n = 1000
+    for bits in (4, 8, 3):
+        qw = q.quantize(synth.normal_weight(n, k, 0.02, seed=bits + k).to(dev), gs, bits, "bf16")
+        x = synth.normal_x((32, 1, k), "bf16", seed=bits).to(dev)
+        singles = [q.qmv(x[i], qw) for i in range(32)]
+        for b in (1, 2, 16, 17, 32):
+            y = q.qmv(x[:b], qw)
+            for i in range(b):
+                assert torch.equal(y[i], singles[i]), (bits, b, i)
+        assert torch.equal(q.qmv(x, qw, flags=q.QMM_FLAG_FORCE_STRIDED), q.qmv(x, qw))
+        buf = synth.normal_x((64, k), "bf16", seed=99).to(dev)
+        assert torch.equal(q.qmv(buf[0::2], qw), q.qmv(buf[0::2].contiguous(), qw))
+        assert_close(q.qmv(x, qw).view(32, n), reference_rows(values(x).reshape(32, k), qw, "bf16"),
+                     "bits=%d" % bits)
 
 
 @pytest.mark.parametrize("bits,extra", [(3, 1), (5, 3), (6, 2), (2, 2), (4, 4)])
@@ -121,19 +126,33 @@ def test_full_size_unaligned_sampled(dev):
         assert_close(y[: min(m, 8), rows], reference_rows(xm, qw, "bf16", rows=rows), "m=%d" % m)
 
 
-def test_decode_only_entries_reject_unaligned(dev):
+def test_gathered_and_argmax_at_unaligned_k(dev):
+    """The gathered and argmax decode forms run at unaligned K (equal to qmv per row); rows
+    padded to a word count the decode kernels cannot take are refused there."""
     import bit_affine_quantized_qmv_amd as q
-    k = 1056
-    qw = q.quantize(synth.normal_weight(64, k, 0.5, seed=1).to(dev), 32, 4, "bf16")
-    x = synth.normal_x((2, k), "bf16", seed=2).to(dev)
-    with pytest.raises(q.QmmError) as e:
-        q.qmv_argmax(x, qw)
-    assert e.value.code == -5
-    ex = q.ExpertWeights.stack([qw, qw])
-    with pytest.raises(q.QmmError) as e:
-        q.gather_qmv(x, ex, torch.zeros(2, dtype=torch.int32, device=dev))
-    assert e.value.code == -5
+    k, n = 1056, 700
+    qa = q.quantize(synth.normal_weight(n, k, 0.5, seed=1).to(dev), 32, 4, "bf16")
+    qb = q.quantize(synth.normal_weight(n, k, 0.5, seed=2).to(dev), 32, 4, "bf16")
+    x = synth.normal_x((5, k), "bf16", seed=2).to(dev)
+    idx, val, y = q.qmv_argmax(x, qa)
+    assert torch.equal(y, q.qmv(x, qa))
+    assert torch.equal(idx, torch.argmax(y.float(), dim=1).to(torch.int32))
+    ex = q.ExpertWeights.stack([qa, qb])
+    sel = torch.tensor([1, 0, 1, 1, 0], dtype=torch.int32, device=dev)
+    yg = q.gather_qmv(x, ex, sel)
+    for r, e in enumerate(sel.tolist()):
+        assert torch.equal(yg[r], q.qmv(x[r:r + 1], (qa, qb)[e])[0]), r
     aligned = q.quantize(synth.normal_weight(64, 1024, 0.5, seed=1).to(dev), 32, 3, "bf16")
     with pytest.raises(q.QmmError) as e:
         q.qmv_argmax(synth.normal_x((2, 1024), "bf16", seed=2).to(dev), _padded(aligned, 1))
+    assert e.value.code == -5
+    words = aligned.w_packed.shape[1]
+    wp = torch.zeros(2, 64, words + 1, dtype=torch.int32, device=dev)[:, :, :words]
+    wp[0] = aligned.w_packed
+    wp[1] = aligned.w_packed
+    ex_odd = q.ExpertWeights(wp, torch.stack([aligned.scales] * 2), torch.stack([aligned.biases] * 2), 64, 1024,
+                             32, 3)
+    with pytest.raises(q.QmmError) as e:
+        q.gather_qmv(synth.normal_x((2, 1024), "bf16", seed=2).to(dev), ex_odd,
+                     torch.zeros(2, dtype=torch.int32, device=dev))
     assert e.value.code == -5
