@@ -233,10 +233,11 @@ def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
     dy = torch.empty(32, 1, un, dtype=ux.dtype, device=dev)
     tdd = _time_steps(lambda i: q.qmv(dx, uq, out=dy), nsteps, nwarm, torch, not args.no_graph)
     ubytes = un * uk * uc["bits"] // 8 + 2 * un * (uk // uc["group_size"]) * 2 + 32 * uk * 2 + 32 * un * 2
-    res["unaligned_k"]["decode_32_rows"] = {
-        "kernel_ms_mean": round(tdd["kernel_mean_ms"], 5),
-        "effective_GBps": round(ubytes / (tdd["kernel_mean_ms"] * 1e-3) / 1e9, 1),
-        "note": "x [32,1,4128]: runs the MFMA kernel (the decode kernels take K a multiple of 128)"}
+    res["unaligned_k"]["decode_32_rows"] = _leg(
+        "unaligned-K qmv effective HBM GB/s", ubytes, tdd, "hbm", "GB/s", HBM_PEAK_GBS, "qmv_parts_kernel",
+        {"workload": "decode qmv at unaligned K: x [32,1,4128] bf16 against the same W [14336,4128] 4-bit group 32 "
+                     "(last slot masked, rows cut into 4 parts along K, two 16-row passes)",
+         "algorithmic_bytes_per_call": ubytes})
     del uq, ux, uy, dx, dy
 
 

@@ -311,15 +311,16 @@ __device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb
 
 template <class T, int BITS, int MROWS>
 __device__ inline void stage_x_issue(XStage<MROWS>& st, const uint16_t* xr, int k_begin, int k_len, int batch,
-                                     int tid, int nthreads) {
+                                     int tid, int nthreads, int rows) {
   const int c8 = k_len >> 3;
   const int per = nthreads / MROWS;       // chunks advanced per pass
   const int j0 = tid / MROWS + batch * kStageBatch * per;
+  const bool live = tid % MROWS < rows;   // padding rows are stored as zero without a load
 #pragma unroll
   for (int b = 0; b < kStageBatch; ++b) {
     int j8 = j0 + b * per;
     j8 = j8 < c8 ? j8 : 0;
-    st.v[b] = *(const u32x4*)(xr + k_begin + 8 * j8);
+    st.v[b] = live ? *(const u32x4*)(xr + k_begin + 8 * j8) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -368,7 +369,7 @@ __device__ inline void stage_x(u32x4* xs, const MatArgs& a, const uint16_t* xb, 
   const int nb = stage_batches<MROWS>(k_len, nthreads);
   for (int batch = 0; batch < nb; ++batch) {
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, k_begin, k_len, batch, tid, nthreads);
+    stage_x_issue<T, BITS, MROWS>(st, xr, k_begin, k_len, batch, tid, nthreads, rows);
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, k_len, batch, tid, nthreads);
   }
 }
@@ -448,6 +449,30 @@ template <int GS>
 __device__ inline int bias_span(int slots_per_row) {
   return (QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
 }
+
+// Parts per row: the largest power of two <= min(8, slots/8), at least 1 (rows of at most
+// 15 slots are not cut).  A function of K, the code width and the group size only, so every
+// decode kernel sums a row the same way: part sums in k order, then added part by part.
+template <int BITS, int GS>
+__host__ __device__ inline int row_parts(int64_t K) {
+  const int64_t nit = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan;
+  int p = 1;
+  while (p < 8 && 2 * p * 8 <= nit) p *= 2;
+  return p;
+}
+
+// Sub-block size (slots) the decode kernels use for a row of nit slots.
+__host__ __device__ inline int block_slots(int nit) { return (QMM_MAX_BLOCK_SLOTS >= 2 && nit % 2 == 0) ? 2 : 1; }
+
+// Slots per part: the slots rounded up to a multiple of P * D, divided by P (a part may
+// reach past the row's last slot; those slots add nothing).
+template <int BITS, int GS>
+__host__ __device__ inline int part_slots(int64_t K) {
+  const int nit = (int)((K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
+  const int p = row_parts<BITS, GS>(K), d = block_slots(nit);
+  return (nit + p * d - 1) / (p * d) * d;
+}
+
 
 template <class T, int BITS, int GS, int MT, int TN, int NH, bool BIAS = true>
 __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbRegs<NH> (&sc)[TN],

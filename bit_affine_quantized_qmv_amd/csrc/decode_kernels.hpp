@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     // activation loads first, the weight prefetch right behind them (loads return in issue
     // order, so waiting for the activations does not wait for the weights)
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads);
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows);
     // every wave's activation loads are issued before any weight load enters the queue
     if (QMM_EARLY_W >= 2) lds_barrier();
     prefetch();
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   } else {
     for (int batch = 0; batch < nbatch; ++batch) {
       XStage<MROWS> st;
-      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads);
+      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads, rows);
       stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
     }
     zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
@@ -426,6 +426,11 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     }
 
   const int nit_total = (K + S::kSpan - 1) / S::kSpan;   // the last slot may end past K
+  // rows cut into parts (see row_parts): part sums added in part order, as the parts kernel does
+  const int n_parts = row_parts<BITS, GS>(K);
+  const int spp = part_slots<BITS, GS>(K);
+  bool have_total = false;
+  f32x4 total[TN][MT];
   const bool pair_bias = bias_span<GS>(nit_total) == 2;
   SbRegs<S::kGroups> b_first[TN];   // bias halfwords of the first slot of a bias pair
   SlotData<BITS, GS> cur[TN], nxt[TN];
@@ -472,9 +477,27 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
           }
         }
       }
+      if (n_parts > 1 && (kit + 1) % spp == 0) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            total[t][mt] = have_total ? total[t][mt] + acc[t][mt] : acc[t][mt];
+            acc[t][mt] = zero4;
+          }
+        have_total = true;
+      }
 #pragma unroll
       for (int t = 0; t < TN; ++t) cur[t] = nxt[t];
     }
+  }
+  if (n_parts > 1) {
+    // the last part ends past the row's slots when they are not a whole number of parts
+    const bool open_part = nit_total % spp != 0;
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = open_part ? total[t][mt] + acc[t][mt] : total[t][mt];
   }
   if (wb.bad) {
 #pragma unroll
@@ -500,6 +523,14 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     argmax_complete(a, a.batches * rows, (unsigned*)kl);   // kl is free again after the barrier inside
   }
 }
+
+}  // namespace decode
+}  // namespace qmm
+
+#include "decode_parts.hpp"
+
+namespace qmm {
+namespace decode {
 
 // ----------------------------------------------------------------------------- launchers
 int device_cus();
@@ -561,6 +592,54 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
   return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
 }
 
+template <class T, int BITS, int GS, int MT, int D, bool SBB>
+hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P, int spp) {
+  auto kern = qmv_parts_kernel<T, BITS, GS, MT, D, SBB>;
+  static int per_cu = -1;
+  static int lds_cached = -1;
+  if (lds_cached != lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kStreamThreads, lds);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+    lds_cached = lds;
+  }
+  const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
+  const int64_t groups = kStreamWaves / P;
+  const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
+  const int64_t blocks = std::min<int64_t>(full, (n_pairs + groups - 1) / groups);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a, P,
+                     spp);
+  return hipGetLastError();
+}
+
+template <class T, int BITS, int GS, int MT>
+hipError_t launch_parts(const MatArgs& a, hipStream_t stream, int lds) {
+  const int P = row_parts<BITS, GS>(a.K);
+  const int spp = part_slots<BITS, GS>(a.K);
+  const int nit = (int)((a.K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
+  if (block_slots(nit) == 2) {
+    if constexpr (BITS == 4 || BITS == 8) {
+      constexpr int bytes = 2 * Slot<BITS, GS>::kGroups * 2;
+      constexpr int align = bytes < 16 ? bytes : 16;
+      if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
+          (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
+        return launch_parts_sb<T, BITS, GS, MT, 2, true>(a, stream, lds, P, spp);
+    }
+    return launch_parts_sb<T, BITS, GS, MT, 2, false>(a, stream, lds, P, spp);
+  }
+  if constexpr (BITS == 4 || BITS == 8) {
+    constexpr int bytes = Slot<BITS, GS>::kGroups * 2;
+    constexpr int align = bytes < 16 ? bytes : 16;
+    if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
+        (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
+      return launch_parts_sb<T, BITS, GS, MT, 1, true>(a, stream, lds, P, spp);
+  }
+  return launch_parts_sb<T, BITS, GS, MT, 1, false>(a, stream, lds, P, spp);
+}
+
 template <class T, int BITS, int GS, int MT>
 hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
   const int64_t rows_per_wg = (int64_t)kWaves * kChunkTiles * 16;
@@ -579,18 +658,21 @@ constexpr int stream_lds_bytes(int K) {
 template <class T, int BITS, int GS>
 hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   const int K = (int)a.K;
-  if (a.rows_per_batch <= 16) {
-    const int lds = stream_lds_bytes<BITS, 1, GS>(K);
-    return lds <= kLdsLimit ? launch_stream<T, BITS, GS, 1>(a, stream, lds) : launch_chunk<T, BITS, GS, 1>(a, stream);
-  }
-  const int lds = stream_lds_bytes<BITS, 2, GS>(K);
-  if (lds <= kLdsLimit) return launch_stream<T, BITS, GS, 2>(a, stream, lds);
+  // long rows (see row_parts) run the parts kernel, the others the streaming kernel
+  const bool parts = row_parts<BITS, GS>(K) > 1;
+  const int lds1 = parts ? parts_lds_bytes<1, GS, BITS>(K) : stream_lds_bytes<BITS, 1, GS>(K);
+  const int lds2 = parts ? parts_lds_bytes<2, GS, BITS>(K) : stream_lds_bytes<BITS, 2, GS>(K);
+  auto run1 = [&](const MatArgs& m) {
+    return parts ? launch_parts<T, BITS, GS, 1>(m, stream, lds1) : launch_stream<T, BITS, GS, 1>(m, stream, lds1);
+  };
+  if (a.rows_per_batch <= 16) return lds1 <= kLdsLimit ? run1(a) : launch_chunk<T, BITS, GS, 1>(a, stream);
+  if (lds2 <= kLdsLimit)
+    return parts ? launch_parts<T, BITS, GS, 2>(a, stream, lds2) : launch_stream<T, BITS, GS, 2>(a, stream, lds2);
   // 17..32 rows whose activations do not fit in LDS at once: when 16 activation rows do,
-  // run the one-block streaming kernel twice (rows 0..15, then the rest), which keeps every
-  // row's arithmetic that of a call of at most 16 rows.  The second pass needs the rows to
+  // run the one-block kernel twice (rows 0..15, then the rest), which keeps every row's
+  // arithmetic that of a call of at most 16 rows.  The second pass needs the rows to
   // continue one 16-row block further at a fixed offset: one segment, or segments that are
   // whole 16-row blocks; one grid slice.
-  const int lds1 = stream_lds_bytes<BITS, 1, GS>(K);
   const int64_t rows = a.rows_per_batch;
   const bool one_seg = a.seg_rows >= rows;
   if (lds1 <= kLdsLimit && a.batches == 1 && (one_seg || a.seg_rows % 16 == 0)) {
@@ -609,9 +691,9 @@ hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
       hi.argmax_index = a.argmax_index + 16;
       if (a.argmax_value) hi.argmax_value = a.argmax_value + 16;
     }
-    hipError_t e = launch_stream<T, BITS, GS, 1>(lo, stream, lds1);
+    hipError_t e = run1(lo);
     if (e != hipSuccess) return e;
-    return launch_stream<T, BITS, GS, 1>(hi, stream, lds1);
+    return run1(hi);
   }
   return launch_chunk<T, BITS, GS, 2>(a, stream);
 }
