@@ -28,7 +28,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-QMV_SOURCES = ["decode.cpp", "decode_b4.hip", "decode_impl.hpp", "decode_kernels.hpp",
+QMV_SOURCES = ["decode.cpp", "decode_b4.hip", "decode_impl.hpp", "decode_kernels.hpp", "decode_parts.hpp",
                "device_common.hpp", "kernels.hpp"]
 QMM_T_SOURCES = ["prefill.hip", "dequant_impl.hpp", "device_common.hpp", "kernels.hpp"]
 
