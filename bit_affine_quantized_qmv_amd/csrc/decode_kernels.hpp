@@ -534,21 +534,14 @@ namespace decode {
 
 // ----------------------------------------------------------------------------- launchers
 int device_cus();
+hipError_t kernel_wgs_per_cu(const void* kern, int threads, int lds, int lds_max, int* out);
 
 template <class T, int BITS, int GS, int MT, int D, bool SBB>
 hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
   auto kern = qmv_stream_kernel<T, BITS, GS, MT, D, SBB>;
-  static int per_cu = -1;  // occupancy for this instantiation (same LDS class each call)
-  static int lds_cached = -1;
-  if (lds_cached != lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kStreamThreads, lds);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-    lds_cached = lds;
-  }
+  int per_cu = 1;
+  const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
+  if (occ != hipSuccess) return occ;
   // one full wave of workgroups (every CU at its occupancy), tile pairs spread over all waves
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
 #ifndef QMM_MAX_WG_PER_CU
@@ -595,17 +588,9 @@ hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
 template <class T, int BITS, int GS, int MT, int D, bool SBB>
 hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P, int spp) {
   auto kern = qmv_parts_kernel<T, BITS, GS, MT, D, SBB>;
-  static int per_cu = -1;
-  static int lds_cached = -1;
-  if (lds_cached != lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kStreamThreads, lds);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-    lds_cached = lds;
-  }
+  int per_cu = 1;
+  const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
+  if (occ != hipSuccess) return occ;
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
   const int64_t groups = kStreamWaves / P;
   const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);

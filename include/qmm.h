@@ -9,8 +9,9 @@
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers.  Descriptors are HOST pointers, read during the
- *     call only.  The caller owns all memory; the library allocates nothing and keeps no
- *     state besides a thread-local error message.
+ *     call only.  The caller owns all memory; the library allocates no device memory.  Its
+ *     host state is a thread-local error message and, per device, cached launch settings
+ *     (kernel LDS limits, occupancies), guarded so that calls from several threads are safe.
  *   - Strides are in elements.  A tensor pointer points at the view's first element (a view's
  *     storage offset is already applied).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued asynchronously;

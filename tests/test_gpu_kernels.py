@@ -261,3 +261,39 @@ def test_large_k_seventeen_to_32_rows(dev):
     idx, val, yl = q.qmv_argmax(x[:20], qw)
     assert torch.equal(yl, singles[:20])
     assert torch.equal(idx, torch.argmax(yl.float(), dim=1).to(torch.int32))
+
+
+def test_concurrent_calls_from_threads(dev):
+    """Calls from several host threads, each on its own stream and with its own shape (so
+    different launch settings are looked up at once), give the sequential results."""
+    import threading
+    import bit_affine_quantized_qmv_amd as q
+    cases = []
+    for i, (k, n, m, bits) in enumerate([(1024, 3000, 32, 4), (2048, 1500, 8, 4), (4096, 700, 1, 8), (1056, 900, 20, 4)]):
+        qw = q.quantize(synth.normal_weight(n, k, 0.02, seed=60 + i).to(dev), 32, bits, "bf16")
+        x = synth.normal_x((m, k), "bf16", seed=70 + i).to(dev)
+        cases.append((qw, x, q.qmv(x, qw)))
+    torch.cuda.synchronize()
+    outs = [None] * len(cases)
+    errors = []
+
+    def work(j):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                qw, x, _ = cases[j]
+                ys = [q.qmv(x, qw) for _ in range(20)]
+            s.synchronize()
+            outs[j] = ys
+        except Exception as e:          # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for j, (_, _, ref) in enumerate(cases):
+        for y in outs[j]:
+            assert torch.equal(y, ref), j
