@@ -226,7 +226,7 @@ def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
     flops = 2.0 * uc["b"] * uc["s"] * un * uk
     tu = _time_steps(lambda i: q.qmm_t(ux, uq, out=uy), max(10, nsteps // 2), nwarm, torch, not args.no_graph)
     res["unaligned_k"] = _leg(
-        "unaligned-K qmm_t TFLOP/s", flops, tu, "mfma", "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "qmm_prefill_kernel",
+        "unaligned-K qmm_t TFLOP/s", flops, tu, "mfma", "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "qmm_prefill_dma_kernel",
         {"workload": "prefill qmm_t at unaligned K: x [4,512,4128] bf16, W [14336,4128] 4-bit group 32 "
                      "bf16 (last k step of 32)", "flops_per_call": flops})
     dx = ux[0, :32].contiguous().view(32, 1, uk)
@@ -403,8 +403,8 @@ def main():
                        "narrowed_view_kernel_ms": round(pv["kernel_mean_ms"], 5)},
             "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": _traffic("qmm_prefill_kernel_prefill_traffic.md", QMM_T_SOURCES),
-                         "kernel": "qmm_prefill_kernel", "kernel_ms_mean": round(pt["kernel_mean_ms"], 5),
+                         "traffic": _traffic("qmm_prefill_dma_kernel_prefill_traffic.md", QMM_T_SOURCES),
+                         "kernel": "qmm_prefill_dma_kernel", "kernel_ms_mean": round(pt["kernel_mean_ms"], 5),
                          "kernel_ms_median": round(pt["kernel_median_ms"], 5)},
         }
         del pqs, pxs, pys, buf, pw

@@ -7,6 +7,11 @@
 // output row through the plan's row addressing, which also serves strided batches such as
 // a view narrowed on the sequence dimension (transformers issue 47331, layout table: every
 // row of every batch element must be computed).
+//
+// Two kernels share this arithmetic and the 256 x 256 x 64 tiling.  qmm_prefill_kernel
+// stages the activation tile through registers.  qmm_prefill_dma_kernel (4-bit codes)
+// moves it with direct global-to-LDS loads a whole step ahead, and keeps the weight codes
+// of two steps in registers, so both loads have a full step of MFMAs to land behind.
 #include "dequant_impl.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -170,13 +175,209 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs 
       }
 }
 
+// Source of the activation chunks that lie past the call's rows or past K: the direct
+// global-to-LDS loads cannot zero a lane, so such lanes read this zero chunk instead.
+__device__ const u32x4 kZeroChunk = {0u, 0u, 0u, 0u};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <class T, int BITS>
+__global__ __launch_bounds__(kThreads, 1) void qmm_prefill_dma_kernel(const MatArgs a, const int m_tiles) {
+  // Activation tile: row-major, 256 rows x 64 k (eight 16-byte chunks per row); chunk c of
+  // row r sits at position c ^ ((r >> 1) & 7), so the 16 rows one MFMA operand read touches
+  // fall in distinct LDS banks.  It is filled by direct global-to-LDS loads: one 64-lane
+  // load writes 1 KB of LDS (8 whole rows), reading 8 whole 128-byte lines of x.
+  // Weight tile: [k half (32)][lane group (8 k)][row] of 8 dequantized values.
+  // Separate arrays per buffer let the compiler see that reading one buffer does not
+  // depend on the direct loads still landing in the other.
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
+  __shared__ u32x4 Bs0[BK / 32][4][BN], Bs1[BK / 32][4][BN];
+  constexpr int TM = BM / WM, TN = BN / WN;      // wave tile
+  constexpr int FM = TM / 16, FN = TN / 16;      // 16x16 MFMA blocks per wave tile
+  constexpr int A_LOADS = BM * 8 / 64 / (kThreads / 64);   // 64-lane activation loads per wave
+  static_assert(BN * 2 == kThreads, "one thread per 32 codes of a weight row");
+  static_assert(FM == 4 && A_LOADS == 4, "tile shape");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4;
+  const int col = lane & 15;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  // M-tile fastest: consecutive workgroups (which the dispatcher spreads over the XCDs)
+  // share a weight tile, and each XCD keeps seeing the same activation rows
+  const int mt = (int)(blockIdx.x % (unsigned)m_tiles);
+  const int nt = (int)(blockIdx.x / (unsigned)m_tiles);
+  const int64_t z = blockIdx.z;
+  const int64_t rows = a.rows_per_batch;
+  const int64_t N = a.N;
+  const int K = (int)a.K;
+  const int gs_shift = __builtin_ctz((unsigned)a.group_size);   // group sizes are powers of two
+  const int64_t bm0 = (int64_t)mt * BM;
+  const int64_t bn0 = (int64_t)nt * BN;
+  const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
+
+  // activation loads: load j of this wave covers tile rows r0 = 8 * (4 * wave + j) .. r0 + 7;
+  // lane i fills position i % 8 of row r0 + i / 8, i.e. logical chunk (i % 8) ^ ((r >> 1) & 7)
+  const uint16_t* asrc[A_LOADS];
+  int ak[A_LOADS];
+  bool arow_ok[A_LOADS];
+#pragma unroll
+  for (int j = 0; j < A_LOADS; ++j) {
+    const int r = 8 * (A_LOADS * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t m = bm0 + r;
+    arow_ok[j] = m < rows;
+    const int64_t mr = m < rows ? m : 0;
+    ak[j] = 8 * c;
+    asrc[j] = xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride + 8 * c;
+  }
+  // When K is not a multiple of BK the last step is partial: activation chunks at k >= K
+  // read the zero chunk, and code runs at k >= K read the row's first run and are zeroed (K
+  // is a multiple of 32, so a chunk or run is either wholly inside or wholly outside the row).
+  auto load_a = [&](int kt, u32x4* dst) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      const bool ok = arow_ok[j] && k0 + ak[j] < K;
+      const void* src = ok ? (const void*)(asrc[j] + k0) : (const void*)&kZeroChunk;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + 64 * (A_LOADS * wave + j)), 16, 0, 0);
+    }
+  };
+  // weight: thread -> row wr, 32-code half wh of the 64 k of a step
+  const int wr = tid >> 1, wh = tid & 1;
+  const int64_t wn_row = bn0 + wr < N ? bn0 + wr : N - 1;
+  const uint32_t* wrow = a.w + wn_row * a.w_row_stride;
+  const uint16_t* srow = (const uint16_t*)a.scales + wn_row * a.sb_row_stride;
+  const uint16_t* brow = (const uint16_t*)a.biases + wn_row * a.sb_row_stride;
+  // two register sets of weight codes, scale and bias, used by alternate steps
+  uint32_t rwA[BITS], rwB[BITS];
+  uint32_t rsA = 0, rbA = 0, rsB = 0, rbB = 0;
+  // (a run at k >= K reads the row's first run; its scale and bias are zeroed at use)
+  auto load_w = [&](int kt, uint32_t(&rw)[BITS], uint32_t& rs, uint32_t& rb) {
+    const int kw = kt * BK + 32 * wh;
+    const bool wv_ok = kw < K;
+    load_codes<BITS>(rw, wrow + (wv_ok ? kw / 32 * BITS : 0));
+    const int g = wv_ok ? kw >> gs_shift : 0;
+    rs = srow[g];
+    rb = brow[g];
+  };
+  // w~ of the run loaded for step kt, zero past K
+  auto dequant_w = [&](int kt, const uint32_t(&rw)[BITS], uint32_t rs, uint32_t rb, u32x4(&wv)[4]) {
+    const bool wv_ok = kt * BK + 32 * wh < K;
+    dequant32<T, BITS>(rw, wv_ok ? T::to_f32(rs) : 0.f, wv_ok ? T::to_f32(rb) : 0.f, wv);
+  };
+
+  f32x4 acc[FM][FN];
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero4;
+
+  // MFMA operand positions: row R = wm * TM + 16 * i + col has (R >> 1) & 7 == col >> 1
+  const int aswz = col >> 1;
+  const int nk = (K + BK - 1) / BK;
+
+  // One k step.  The MFMAs read buffer `cur`; the weights of step kt+1 (registers rw/rs/rb,
+  // loaded two steps earlier) are dequantized and written to the other buffer between the
+  // first half of the MFMAs, and the activations of step kt+1 land there through direct
+  // loads issued right after that dequantization; the weight registers are refilled with
+  // step kt+3 at the end of the step.
+  // Before the barrier every load of this wave older than that refill has landed (the
+  // direct loads included), so one barrier per step orders everything.
+  auto step = [&](int kt, u32x4* Acur, u32x4* Anxt, u32x4(&Bcur)[BK / 32][4][BN], u32x4(&Bnxt)[BK / 32][4][BN],
+                  uint32_t(&rw)[BITS], uint32_t& rs, uint32_t& rb) {
+    typename T::v8 av[FM], bv[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) av[i] = as_v8<T>(Acur[(wm * TM + 16 * i + col) * 8 + (lg ^ aswz)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[j] = as_v8<T>(Bcur[0][lg][wn * TN + 16 * j + col]);
+    // The weight registers are read through an opaque zero made here, so no use of them is
+    // moved above the previous step's barrier, where it would wait for the loads still
+    // landing (the other register set's, and the direct activation loads).
+    uint32_t opq;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
+    uint32_t rwo[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) rwo[i] = rw[i] ^ opq;
+    u32x4 wv[4];
+    dequant_w(kt + 1, rwo, rs ^ opq, rb ^ opq, wv);
+    load_a(kt + 1, Anxt);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
+      Bnxt[wh][i][wr] = wv[i];
+    }
+#pragma unroll
+    for (int t = 0; t < FM * FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+      if (t % 8 == 7) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) av[i] = as_v8<T>(Acur[(wm * TM + 16 * i + col) * 8 + ((4 + lg) ^ aswz)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[j] = as_v8<T>(Bcur[1][lg][wn * TN + 16 * j + col]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
+    // vmcnt(0): the direct activation loads of step kt+1 (and the weights of step kt+2)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    load_w(kt + 3, rw, rs, rb);
+    lds_barrier();
+  };
+
+  // prologue: activations and weights of step 0 in buffer 0, weights of steps 1 and 2 in
+  // registers
+  load_w(0, rwA, rsA, rbA);
+  load_a(0, As0);
+  load_w(1, rwB, rsB, rbB);
+  {
+    u32x4 wv[4];
+    dequant_w(0, rwA, rsA, rbA, wv);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Bs0[wh][c][wr] = wv[c];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  load_w(2, rwA, rsA, rbA);
+  lds_barrier();
+  // Steps run in pairs, so that every register set and buffer is named statically; an odd
+  // step count gets one more step whose operands are all zero (activations past K read the
+  // zero chunk, weights past K have zero scale and bias), which adds nothing.
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, As0, As1, Bs0, Bs1, rwB, rsB, rbB);
+    step(kt + 1, As1, As0, Bs1, Bs0, rwA, rsA, rbA);
+  }
+
+  uint16_t* yb = (uint16_t*)a.y + z * rows * N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = bm0 + wm * TM + 16 * i + 4 * lg + r;
+        const int64_t n = bn0 + wn * TN + 16 * j + col;
+        if (m < rows && n < N) yb[m * N + n] = T::from_f32(acc[i][j][r]);
+      }
+}
+
 template <class T, int BITS>
 hipError_t launch_bits(const MatArgs& a, hipStream_t stream) {
   const int64_t m_tiles = (a.rows_per_batch + BM - 1) / BM;
   const int64_t n_tiles = (a.N + BN - 1) / BN;
   if (m_tiles * n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), dim3((unsigned)(m_tiles * n_tiles), 1, (unsigned)a.batches),
-                     dim3(kThreads), 0, stream, a, (int)m_tiles);
+  const dim3 grid((unsigned)(m_tiles * n_tiles), 1, (unsigned)a.batches);
+  // 4-bit codes take the kernel with direct activation loads; at the other widths its
+  // register budget (256 per lane at two waves per SIMD) does not hold without spills
+  if constexpr (BITS == 4)
+    hipLaunchKernelGGL((qmm_prefill_dma_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
+  else
+    hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
   return hipGetLastError();
 }
 
