@@ -359,3 +359,31 @@ def argmax_acceptable(y_ref, tol) -> list:
     tol = np.asarray(tol, dtype=np.float64)
     floor = (y_ref - tol).max(axis=1, keepdims=True)
     return [set(np.nonzero(row)[0].tolist()) for row in (y_ref + tol >= floor)]
+
+
+# ----------------------------------------------------------------------------------
+# per-row top-k of the logits
+# ----------------------------------------------------------------------------------
+def topk_rows(y_bits, k: int, dtype: str):
+    """The k largest logits of each row, largest first, from logits held as storage-dtype
+    bit patterns (what the decode kernel returns).  Order: larger value first; NaN above
+    every number (as the fused argmax counts it); +0 above -0; equal values by lower column
+    first, so k = 1 gives the argmax contract's first maximal column.
+    Returns (index int64 [rows, k], value float64 [rows, k])."""
+    vals = from_dtype_bits(np.asarray(y_bits), dtype)
+    rows, n = vals.shape
+    idx = np.zeros((rows, k), dtype=np.int64)
+    out = np.zeros((rows, k), dtype=np.float64)
+    for r in range(rows):
+        row = vals[r]
+
+        def rank(j):
+            v = row[j]
+            if np.isnan(v):
+                return (0, 0.0, 0, j)
+            return (1, -v, 1 if (v == 0 and np.signbit(v)) else 0, j)
+
+        order = sorted(range(n), key=rank)[:k]
+        idx[r] = order
+        out[r] = row[order]
+    return idx, out

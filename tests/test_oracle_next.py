@@ -91,3 +91,49 @@ def test_argmax_acceptable_exact_and_ties():
     # tolerance widens the set to the values that could overtake the maximum
     got = O.argmax_acceptable(y, np.full_like(y, 0.3))
     assert got == [{1, 3}, {1, 3}]
+
+
+def _bits(vals, dtype="bf16"):
+    return O.to_dtype_bits(np.asarray(vals, dtype=np.float32), dtype)
+
+
+def test_topk_matches_descending_sort():
+    # distinct values: the order is the plain descending sort
+    rng = np.random.default_rng(7)
+    v = rng.permutation(np.arange(-40, 40, dtype=np.float32))[None, :] * 0.25
+    for dtype in ("bf16", "fp16"):
+        idx, val = O.topk_rows(_bits(v, dtype), 9, dtype)
+        want = np.argsort(-v[0], kind="stable")[:9]
+        assert idx[0].tolist() == want.tolist()
+        assert val[0].tolist() == sorted(v[0].tolist(), reverse=True)[:9]
+
+
+def test_topk_ties_take_lower_columns_first():
+    idx, val = O.topk_rows(_bits([[1.0, 3.0, 3.0, 2.0, 3.0, 2.0]]), 4, "bf16")
+    assert idx[0].tolist() == [1, 2, 4, 3]
+    assert val[0].tolist() == [3.0, 3.0, 3.0, 2.0]
+
+
+def test_topk_nan_infinities_and_signed_zero():
+    row = np.array([[0.0, -0.0, np.nan, np.inf, -np.inf, 1.0, -2.0]], dtype=np.float16)
+    idx, val = O.topk_rows(row.view(np.uint16), 7, "fp16")   # exact fp16 patterns
+    assert idx[0].tolist() == [2, 3, 5, 0, 1, 6, 4]
+    assert np.isnan(val[0, 0]) and val[0, 1] == np.inf and val[0, -1] == -np.inf
+    assert not np.signbit(val[0, 3]) and np.signbit(val[0, 4])
+
+
+def test_topk_k1_is_first_maximal_column():
+    rng = np.random.default_rng(3)
+    v = rng.integers(-3, 4, size=(6, 40)).astype(np.float32)   # many ties
+    idx, val = O.topk_rows(_bits(v), 1, "bf16")
+    for r in range(6):
+        assert idx[r, 0] == int(np.argmax(v[r])) and val[r, 0] == v[r].max()
+
+
+def test_topk_full_k_is_a_permutation():
+    rng = np.random.default_rng(5)
+    v = rng.integers(-5, 5, size=(3, 33)).astype(np.float32)
+    idx, val = O.topk_rows(_bits(v), 33, "bf16")
+    for r in range(3):
+        assert sorted(idx[r].tolist()) == list(range(33))
+        assert all(val[r, j] >= val[r, j + 1] for j in range(32))
