@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
 # Every symbol include/qmm.h declares.
 EXPORTS = ("qmm_abi_version", "qmm_last_error", "qmm_quantize", "qmv", "qmm_t", "qmm_plan", "qmm_gather_qmv",
-           "qmm_dequantize", "qmm_embedding", "qmm_qmv_argmax")
+           "qmm_dequantize", "qmm_embedding", "qmm_qmv_argmax", "qmm_topk", "qmm_qmv_topk")
 
 
 class TensorDesc(ctypes.Structure):
@@ -96,6 +96,12 @@ def load() -> ctypes.CDLL:
     lib.qmm_qmv_argmax.restype = ctypes.c_int32
     lib.qmm_qmv_argmax.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), P,
                                    ctypes.POINTER(TensorDesc), P, P, P, P]
+    lib.qmm_topk.restype = ctypes.c_int32
+    lib.qmm_topk.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                             P, P, P]
+    lib.qmm_qmv_topk.restype = ctypes.c_int32
+    lib.qmm_qmv_topk.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), P,
+                                 ctypes.POINTER(TensorDesc), ctypes.c_int32, P, P, P]
     lib.qmm_dequantize.restype = ctypes.c_int32
     lib.qmm_dequantize.argtypes = [ctypes.POINTER(WeightDesc), P, ctypes.c_int64, P]
     lib.qmm_embedding.restype = ctypes.c_int32

@@ -176,6 +176,52 @@ def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, worksp
     return idx, val, y
 
 
+def _dtype_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _lib.QMM_BF16
+    if dtype == torch.float16:
+        return _lib.QMM_FP16
+    raise _lib.QmmError(-2, "logits must be bfloat16 or float16")
+
+
+def topk(logits: torch.Tensor, k: int, out_index=None, out_value=None):
+    """Per-row top-k of a [rows, n] logits tensor (qmm_topk): (index int32 [rows, k], value
+    float32 [rows, k]), largest first, equal values by lower column."""
+    lib = _lib.load()
+    assert logits.dim() == 2 and logits.stride(1) == 1
+    rows, n = logits.shape
+    idx = out_index if out_index is not None else torch.empty(rows, k, dtype=torch.int32, device=logits.device)
+    val = out_value if out_value is not None else torch.empty(rows, k, dtype=torch.float32, device=logits.device)
+    assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows * k
+    assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows * k
+    _lib.check(lib.qmm_topk(logits.data_ptr(), _dtype_code(logits.dtype), rows, n, logits.stride(0) if rows else n,
+                            k, idx.data_ptr(), val.data_ptr(), _stream(logits.device)))
+    return idx, val
+
+
+def qmv_topk(x: torch.Tensor, qw: QuantizedWeight, k: int, out=None, out_index=None, out_value=None):
+    """Decode qmv followed by a per-row top-k of its logits (qmm_qmv_topk).  Returns
+    (index int32 [rows, k], value float32 [rows, k], y)."""
+    lib = _lib.load()
+    rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
+    if out is not None:
+        y = out
+        assert y.dtype == x.dtype and y.is_contiguous() and tuple(y.shape) == tuple(x.shape[:-1]) + (qw.N,)
+    else:
+        y = torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device)
+    idx = out_index if out_index is not None else torch.empty(rows, k, dtype=torch.int32, device=x.device)
+    val = out_value if out_value is not None else torch.empty(rows, k, dtype=torch.float32, device=x.device)
+    assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows * k
+    assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows * k
+    if x.dtype != qw.dtype:
+        raise _lib.QmmError(-2, "x, scales and biases must share one dtype")
+    xd = _lib.tensor_desc(x.shape, x.stride())
+    yd = _lib.tensor_desc(y.shape, y.stride())
+    _lib.check(lib.qmm_qmv_topk(x.data_ptr(), ctypes.byref(xd), ctypes.byref(qw.desc()), y.data_ptr(),
+                                ctypes.byref(yd), k, idx.data_ptr(), val.data_ptr(), _stream(x.device)))
+    return idx, val, y
+
+
 def dequantize(qw: QuantizedWeight, out=None) -> torch.Tensor:
     """Dense [N, K] dtype matrix of the quantized weight (qmm_dequantize)."""
     lib = _lib.load()

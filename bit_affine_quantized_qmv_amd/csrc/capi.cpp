@@ -57,9 +57,53 @@ int32_t run_matmul(const void* x, const qmm_tensor_desc_t* xd, const qmm_weight_
   return launch_status(p.family == 0 ? qmm::launch_decode(a, s) : qmm::launch_prefill(a, s));
 }
 
+// Validation of a top-k call over logits rows (shared by the two top-k entry points).
+int32_t check_topk(int32_t dtype, int64_t n, int64_t row_stride, int32_t k) {
+  if (dtype != QMM_BF16 && dtype != QMM_FP16) return finish(QMM_ERR_UNSUPPORTED, "topk: dtype must be QMM_BF16 or QMM_FP16");
+  if (n <= 0 || n >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "topk: need 0 < n < 2^31");
+  if (row_stride < n) return finish(QMM_ERR_SHAPE, "topk: row_stride < n");
+  if (k < 1 || k > QMM_TOPK_MAX || k > n) return finish(QMM_ERR_SHAPE, "topk: need 1 <= k <= min(n, QMM_TOPK_MAX)");
+  return QMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int64_t row_stride, int32_t k,
+                 int32_t* out_index, float* out_value, void* stream) {
+  if (rows < 0) return finish(QMM_ERR_SHAPE, "topk: rows must be >= 0");
+  const int32_t rc = check_topk(dtype, n, row_stride, k);
+  if (rc != QMM_OK) return rc;
+  if (rows == 0) return finish(QMM_OK, "");
+  if (rows >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "topk: rows must be < 2^31");
+  if (!logits || !out_index) return finish(QMM_ERR_NULL, "topk: logits and out_index must be non-NULL");
+  if ((uintptr_t)logits % 2 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
+    return finish(QMM_ERR_ALIGN, "topk: logits must be 2-byte, out_index/out_value 4-byte aligned");
+  const qmm::TopkArgs a{logits, rows, n, row_stride, k, dtype, out_index, out_value};
+  return launch_status(qmm::launch_topk(a, (hipStream_t)stream));
+}
+
+int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                     const qmm_tensor_desc_t* y_desc, int32_t k, int32_t* out_index, float* out_value,
+                     void* stream) {
+  std::string err;
+  qmm_plan_t p;
+  int rc = qmm::plan_matmul(x, x_desc, w, y, y_desc, 0, 0, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0) return finish(QMM_OK, "");
+  rc = check_topk(w->dtype, w->N, w->N, k);
+  if (rc != QMM_OK) return rc;
+  if (!out_index) return finish(QMM_ERR_NULL, "qmv_topk: out_index must be non-NULL");
+  if ((uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
+    return finish(QMM_ERR_ALIGN, "qmv_topk: out_index/out_value must be 4-byte aligned");
+  const qmm::MatArgs a = make_args(x, p, w, y);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = p.family == 0 ? qmm::launch_decode(a, s) : qmm::launch_prefill(a, s);
+  if (e != hipSuccess) return launch_status(e);
+  const qmm::TopkArgs t{y, p.rows, w->N, w->N, k, w->dtype, out_index, out_value};
+  return launch_status(qmm::launch_topk(t, s));
+}
 
 int32_t qmm_abi_version(void) { return QMM_ABI_VERSION; }
 

@@ -192,6 +192,30 @@ int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
                        const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
                        void* stream);
 
+/* Per-row top-k of stored logits (the top-k form of the decode epilogue on lm_head logits;
+ * transformers issue 47331, "Reproduction": the next-token choice that collapses to token
+ * 0): for every row m and j < k, out_index[m * k + j] and out_value[m * k + j] are the
+ * column and value of the j-th largest entry of logits row m.  Order: larger value first;
+ * NaN counts as larger than any number and +0 as larger than -0; equal values by lower
+ * column, so k = 1 gives the column qmm_qmv_argmax returns.  A NaN entry is reported as a
+ * quiet NaN.
+ * logits: DEVICE [rows, row_stride] of dtype (QMM_BF16 or QMM_FP16), 2-byte aligned,
+ * row_stride >= n.  out_index: DEVICE int32 [rows, k], 4-byte aligned; out_value: DEVICE
+ * float32 [rows, k] or NULL.  Need 0 < n < 2^31, 0 <= rows < 2^31 and
+ * 1 <= k <= min(n, QMM_TOPK_MAX) (QMM_ERR_SHAPE otherwise); rows == 0 is a no-op.
+ * One kernel is enqueued (a workgroup per row); nothing is allocated. */
+#define QMM_TOPK_MAX 1024
+int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int64_t row_stride, int32_t k,
+                 int32_t* out_index, float* out_value, void* stream);
+
+/* Decode with a per-row top-k: y = x . dequant(W)^T exactly as qmv (y is required and
+ * dense, contract as for qmv), then qmm_topk over the rows of y (n = N, row_stride = N)
+ * into out_index / out_value [rows, k].  k is checked before anything is enqueued.
+ * Two kernels are enqueued. */
+int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                     const qmm_tensor_desc_t* y_desc, int32_t k, int32_t* out_index, float* out_value,
+                     void* stream);
+
 /* Dequantize a whole quantized weight to a dense matrix: out[n, k] = RNE_dtype(fl32(fma(s, q, b)))
  * with s, b the (n, k / group_size) scale and bias and q the code (transformers issue 47331,
  * "Root cause": the probe dequantizes the packed weight back to a dense tensor; the

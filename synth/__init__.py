@@ -120,3 +120,9 @@ def rows_sample(n: int, count: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = rng.choice(n, size=min(count, n), replace=False)
     return np.unique(np.concatenate([pick, [0, n - 1]]))
+
+
+def tied_logits(rows: int, n: int, levels: int, dtype: str, seed: int) -> torch.Tensor:
+    """[rows, n] integer-valued logits in [-levels, levels] (many exact ties), in dtype."""
+    v = torch.randint(-levels, levels + 1, (rows, n), generator=_gen(seed), dtype=torch.int64)
+    return v.to(torch.float32).to(torch.bfloat16 if dtype == "bf16" else torch.float16)
