@@ -355,6 +355,29 @@ def main():
                              "4-bit group 64; logits %s" % ("stored" if logits else "not stored"),
                  "algorithmic_bytes_per_call": nbytes})
         out["next"]["qmv_argmax"] = arg_rows
+        # per-row top-k of the lm_head logits: decode then top-k, and the top-k pass alone
+        tk = 50
+        tidx = torch.empty(m, tk, dtype=torch.int32, device=dev)
+        tval = torch.empty(m, tk, dtype=torch.float32, device=dev)
+        tt = _time_steps(lambda i: q.qmv_topk(xs[i % copies], qws[i % copies], tk, out=ys[i % copies],
+                                              out_index=tidx, out_value=tval),
+                         nsteps, nwarm, torch, not args.no_graph)
+        tbytes = qmv_bytes + m * n * 2 + m * tk * 8
+        topk_rows = {"qmv_topk": _leg(
+            "decode + top-k effective HBM GB/s", tbytes, tt, "hbm", "GB/s", HBM_PEAK_GBS,
+            "qmv_stream_kernel + topk_rows_kernel",
+            {"workload": "lm_head decode qmv + per-row top-50: x [32,1,1024] bf16, W [151936,1024] 4-bit "
+                         "group 64; logits stored, then read by the top-k pass",
+             "algorithmic_bytes_per_call": tbytes})}
+        lg = [y.view(m, n) for y in ys]
+        to = _time_steps(lambda i: q.topk(lg[i % copies], tk, out_index=tidx, out_value=tval),
+                         nsteps, nwarm, torch, not args.no_graph)
+        obytes = m * n * 2 + m * tk * 8
+        topk_rows["topk_alone"] = _leg(
+            "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_rows_kernel",
+            {"workload": "per-row top-50 of [32,151936] bf16 logits (one workgroup per row)",
+             "algorithmic_bytes_per_call": obytes})
+        out["next"]["topk"] = topk_rows
         # quantized embedding gather from the lm_head table
         ec = synth.EMBED
         idxs = [synth.token_indices(ec["count"], n, ec["idx_seed"] + c).to(dev) for c in range(copies)]

@@ -6,9 +6,12 @@
 // lm_head exchanges).
 //
 // One 1024-thread workgroup per row, three passes over the row's 16-bit values mapped to
-// order keys (unsigned, larger key = larger value):
-//   1. histogram of the key's high byte -> the bin that holds the k-th largest key;
-//   2. histogram of the low byte inside that bin -> the k-th largest key itself (t) and
+// order keys (unsigned, larger key = larger value), read 8 at a time when the row is
+// 16-byte aligned:
+//   1. histogram of the key's high 11 bits (2048 bins, so that the values of a typical
+//      logit row spread over many LDS counters) -> the bin that holds the k-th largest key,
+//      found with a block-wide suffix count;
+//   2. histogram of the low 5 bits inside that bin -> the k-th largest key itself (t) and
 //      the number of keys above it (g < k);
 //   3. the g keys above t go to candidate slots [0, g) in any order; the first k - g keys
 //      equal to t in column order (a block-wide prefix count over consecutive column runs)
@@ -26,6 +29,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRun = 8;   // consecutive columns per thread in the collecting pass
+constexpr int kCand = 4096;   // candidates the one-pass collection takes
 
 template <bool FP16>
 __device__ inline uint32_t order_key(uint32_t b) {
@@ -60,62 +64,149 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sums,
   return before + s - v;
 }
 
+constexpr int kHiShift = 5;
+constexpr int kHiBins = 1 << (16 - kHiShift);
+constexpr int kLoBins = 1 << kHiShift;
+
+// Calls f(column, key) for every column of the row; each thread takes 8 consecutive
+// columns per step (one 16-byte load when the row is 16-byte aligned).
+template <bool FP16, class F>
+__device__ inline void for_each_key(const uint16_t* row, int64_t n, F&& f) {
+  const bool vec = ((uintptr_t)row & 15u) == 0u;
+  const int64_t n8 = vec ? (n & ~(int64_t)7) : 0;
+  for (int64_t i = (int64_t)threadIdx.x * 8; i < n8; i += (int64_t)kThreads * 8) {
+    const u32x4 v = *(const u32x4*)(row + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f(i + 2 * e, order_key<FP16>(w[e] & 0xFFFFu));
+      f(i + 2 * e + 1, order_key<FP16>(w[e] >> 16));
+    }
+  }
+  for (int64_t i = n8 + threadIdx.x; i < n; i += kThreads) f(i, order_key<FP16>(row[i]));
+}
+
+// Sort the m candidate words cand[0, m) (m <= kCand) descending and store the first k.
+// Padded to a power of two with zero words, which sort below every candidate.
+template <bool FP16>
+__device__ inline void sort_and_store(unsigned long long* cand, uint32_t m, uint32_t k, const TopkArgs& a) {
+  const uint32_t tid = threadIdx.x;
+  uint32_t mp = 1u;
+  while (mp < m) mp <<= 1;
+  __syncthreads();
+  for (uint32_t j = m + tid; j < mp; j += kThreads) cand[j] = 0ull;
+  for (uint32_t size = 2u; size <= mp; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1) {
+      __syncthreads();
+      for (uint32_t i = tid; i < mp; i += kThreads) {
+        const uint32_t j = i ^ stride;
+        if (j > i) {
+          const unsigned long long x = cand[i], y = cand[j];
+          if ((x > y) == ((i & size) == 0u)) {
+            cand[i] = y;
+            cand[j] = x;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (uint32_t j = tid; j < k; j += kThreads) {
+    const unsigned long long c = cand[mp - 1u - j];
+    const uint32_t bits = key_bits((uint32_t)(c >> 32));
+    a.out_index[(int64_t)blockIdx.x * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+    if (a.out_value) a.out_value[(int64_t)blockIdx.x * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
+  }
+}
+
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kHiBins];
   __shared__ uint32_t wave_sums[kWaves];
   __shared__ uint32_t sel[4];
   __shared__ uint32_t n_above_slot;
-  __shared__ unsigned long long cand[kTopkMax];
+  __shared__ unsigned long long cand[kCand];
   const int tid = threadIdx.x;
   const uint16_t* row = (const uint16_t*)a.logits + (int64_t)blockIdx.x * a.row_stride;
   const int64_t n = a.n;
   const uint32_t k = (uint32_t)a.k;
 
-  // 1. high-byte histogram
-  if (tid < 256) hist[tid] = 0u;
+  // 1. histogram of the high bits; the bin of the k-th largest key by a suffix count
+  for (int b = tid; b < kHiBins; b += kThreads) hist[b] = 0u;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kThreads) atomicAdd(&hist[order_key<FP16>(row[i]) >> 8], 1u);
+  for_each_key<FP16>(row, n, [&](int64_t, uint32_t o) { atomicAdd(&hist[o >> kHiShift], 1u); });
   __syncthreads();
-  if (tid == 0) {
-    uint32_t above = 0u;
-    int b = 255;
-    for (; b > 0 && above + hist[b] < k; --b) above += hist[b];
-    sel[0] = (uint32_t)b;
-    sel[1] = above;
+  {
+    static_assert(kHiBins == 2 * kThreads, "two bins per thread");
+    const int b_hi = kHiBins - 1 - 2 * tid, b_lo = b_hi - 1;   // thread 0 holds the top bins
+    const uint32_t c_hi = hist[b_hi], c_lo = hist[b_lo];
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan(c_hi + c_lo, wave_sums, &total);
+    if (above < k && above + c_hi >= k) {
+      sel[0] = (uint32_t)b_hi;
+      sel[1] = above;
+      sel[2] = above + c_hi;
+    } else if (above + c_hi < k && above + c_hi + c_lo >= k) {
+      sel[0] = (uint32_t)b_lo;
+      sel[1] = above + c_hi;
+      sel[2] = above + c_hi + c_lo;
+    }
+    if (tid == 0) n_above_slot = 0u;
   }
   __syncthreads();
   const uint32_t hi = sel[0];
-  // 2. low-byte histogram inside bin hi
-  if (tid < 256) hist[tid] = 0u;
-  __syncthreads();
-  for (int64_t i = tid; i < n; i += kThreads) {
-    const uint32_t o = order_key<FP16>(row[i]);
-    if ((o >> 8) == hi) atomicAdd(&hist[o & 255u], 1u);
+  const uint32_t n_ge = sel[2];   // keys in bin hi or above
+  if (n_ge <= (uint32_t)kCand) {
+    // Usual case: every key in bin hi or above is a candidate (collected in any order; the
+    // sort key carries the column), then sort them all.
+    for_each_key<FP16>(row, n, [&](int64_t i, uint32_t o) {
+      if ((o >> kHiShift) >= hi)
+        cand[atomicAdd(&n_above_slot, 1u)] = ((unsigned long long)o << 32) | (0xFFFFFFFFu - (uint32_t)i);
+    });
+    sort_and_store<FP16>(cand, n_ge, k, a);
+    return;
   }
+  // Otherwise (a huge tie block at the threshold) find the exact k-th key first.
+  // 2. histogram of the low bits inside bin hi
+  if (tid < kLoBins) hist[tid] = 0u;
+  __syncthreads();
+  for_each_key<FP16>(row, n, [&](int64_t, uint32_t o) {
+    if ((o >> kHiShift) == hi) atomicAdd(&hist[o & (kLoBins - 1)], 1u);
+  });
   __syncthreads();
   if (tid == 0) {
     uint32_t above = sel[1];
-    int l = 255;
+    int l = kLoBins - 1;
     for (; l > 0 && above + hist[l] < k; --l) above += hist[l];
-    sel[2] = (hi << 8) | (uint32_t)l;
+    sel[2] = (hi << kHiShift) | (uint32_t)l;
     sel[3] = above;
-    n_above_slot = 0u;
   }
   __syncthreads();
   const uint32_t t = sel[2], g = sel[3], need_eq = k - g;
 
   // 3. collect
+  const bool vec = ((uintptr_t)row & 15u) == 0u;
   uint32_t eq_seen = 0u;   // keys equal to t in earlier runs (the same in every thread)
   for (int64_t base = 0; base < n; base += (int64_t)kThreads * kRun) {
     const int64_t i0 = base + (int64_t)tid * kRun;
     uint32_t o[kRun];
+    if (vec && i0 + kRun <= n) {
+      const u32x4 v = *(const u32x4*)(row + i0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = order_key<FP16>(w[e] & 0xFFFFu);
+        o[2 * e + 1] = order_key<FP16>(w[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRun; ++e) o[e] = i0 + e < n ? order_key<FP16>(row[i0 + e]) : 0u;   // real keys are never 0
+    }
     uint32_t neq = 0u;
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
-      const int64_t i = i0 + e;
-      o[e] = i < n ? order_key<FP16>(row[i]) : 0u;   // keys of real values are never 0
-      if (o[e] > t) cand[atomicAdd(&n_above_slot, 1u)] = ((unsigned long long)o[e] << 32) | (0xFFFFFFFFu - (uint32_t)i);
+      if (o[e] > t)
+        cand[atomicAdd(&n_above_slot, 1u)] = ((unsigned long long)o[e] << 32) | (0xFFFFFFFFu - (uint32_t)(i0 + e));
       neq += o[e] == t ? 1u : 0u;
     }
     uint32_t total;
@@ -129,30 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
     }
     eq_seen += total;
   }
-  // pad to a power of two with words below every candidate, then sort ascending
-  uint32_t kp = 1u;
-  while (kp < k) kp <<= 1;
-  for (uint32_t j = k + tid; j < kp; j += kThreads) cand[j] = 0ull;
-  for (uint32_t size = 2u; size <= kp; size <<= 1) {
-    for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1) {
-      __syncthreads();
-      const uint32_t i = (uint32_t)tid, j = i ^ stride;
-      if (i < kp && j > i) {
-        const unsigned long long x = cand[i], y = cand[j];
-        if ((x > y) == ((i & size) == 0u)) {
-          cand[i] = y;
-          cand[j] = x;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (uint32_t j = tid; j < k; j += kThreads) {
-    const unsigned long long c = cand[kp - 1u - j];
-    const uint32_t bits = key_bits((uint32_t)(c >> 32));
-    a.out_index[(int64_t)blockIdx.x * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-    if (a.out_value) a.out_value[(int64_t)blockIdx.x * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
-  }
+  sort_and_store<FP16>(cand, k, k, a);
 }
 
 }  // namespace
