@@ -115,3 +115,16 @@ def test_qmv_topk_lm_head():
     y2 = y.view(c["m"], c["n"])
     for r in synth.rows_sample(c["m"], 3, seed=1500):
         _check(y2[r:r + 1], idx[r:r + 1], val[r:r + 1], 50, c["dtype"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("levels,k", [(0, 7), (1, 1000), (2, 1024), (3, 1)])
+def test_topk_huge_tie_blocks(levels, k, dtype):
+    # more than 4096 keys at or above the threshold bin: the exact-threshold path, whose
+    # equal keys are taken in column order across many runs of the row
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    logits = synth.tied_logits(3, 20011, levels, dtype, seed=1600 + levels).to(dev)
+    idx, val = q.topk(logits, k)
+    torch.cuda.synchronize()
+    _check(logits, idx, val, k, dtype)
