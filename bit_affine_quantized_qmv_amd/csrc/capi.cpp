@@ -7,6 +7,7 @@
 #include "../../include/qmm.h"
 #include "dispatch.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace {
 

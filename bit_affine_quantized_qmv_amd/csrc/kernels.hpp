@@ -88,18 +88,4 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 // Min/max group quantizer.
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
-// Per-row top-k of stored logits (dtype 1 = bf16, 2 = fp16).
-constexpr int kTopkMax = 1024;
-struct TopkArgs {
-  const void* logits;
-  int64_t rows;
-  int64_t n;            // columns per row
-  int64_t row_stride;   // elements
-  int32_t k;
-  int32_t dtype;
-  int32_t* out_index;   // [rows, k]
-  float* out_value;     // [rows, k] or null
-};
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
-
 }  // namespace qmm

@@ -22,6 +22,7 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace qmm {
 namespace {
