@@ -359,23 +359,24 @@ def main():
         tk = 50
         tidx = torch.empty(m, tk, dtype=torch.int32, device=dev)
         tval = torch.empty(m, tk, dtype=torch.float32, device=dev)
+        tws = q.topk_workspace(m, dev)
         tt = _time_steps(lambda i: q.qmv_topk(xs[i % copies], qws[i % copies], tk, out=ys[i % copies],
-                                              out_index=tidx, out_value=tval),
+                                              out_index=tidx, out_value=tval, workspace=tws),
                          nsteps, nwarm, torch, not args.no_graph)
         tbytes = qmv_bytes + m * n * 2 + m * tk * 8
         topk_rows = {"qmv_topk": _leg(
             "decode + top-k effective HBM GB/s", tbytes, tt, "hbm", "GB/s", HBM_PEAK_GBS,
-            "qmv_stream_kernel + topk_rows_kernel",
+            "qmv_stream_kernel + topk_parts_kernel",
             {"workload": "lm_head decode qmv + per-row top-50: x [32,1,1024] bf16, W [151936,1024] 4-bit "
                          "group 64; logits stored, then read by the top-k pass",
              "algorithmic_bytes_per_call": tbytes})}
         lg = [y.view(m, n) for y in ys]
-        to = _time_steps(lambda i: q.topk(lg[i % copies], tk, out_index=tidx, out_value=tval),
+        to = _time_steps(lambda i: q.topk(lg[i % copies], tk, out_index=tidx, out_value=tval, workspace=tws),
                          nsteps, nwarm, torch, not args.no_graph)
         obytes = m * n * 2 + m * tk * 8
         topk_rows["topk_alone"] = _leg(
-            "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_rows_kernel",
-            {"workload": "per-row top-50 of [32,151936] bf16 logits (one workgroup per row)",
+            "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_parts_kernel",
+            {"workload": "per-row top-50 of [32,151936] bf16 logits (19 column chunks per row)",
              "algorithmic_bytes_per_call": obytes})
         out["next"]["topk"] = topk_rows
         # quantized embedding gather from the lm_head table

@@ -98,10 +98,10 @@ def load() -> ctypes.CDLL:
                                    ctypes.POINTER(TensorDesc), P, P, P, P]
     lib.qmm_topk.restype = ctypes.c_int32
     lib.qmm_topk.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                             P, P, P]
+                             P, P, P, P]
     lib.qmm_qmv_topk.restype = ctypes.c_int32
     lib.qmm_qmv_topk.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(WeightDesc), P,
-                                 ctypes.POINTER(TensorDesc), ctypes.c_int32, P, P, P]
+                                 ctypes.POINTER(TensorDesc), ctypes.c_int32, P, P, P, P]
     lib.qmm_dequantize.restype = ctypes.c_int32
     lib.qmm_dequantize.argtypes = [ctypes.POINTER(WeightDesc), P, ctypes.c_int64, P]
     lib.qmm_embedding.restype = ctypes.c_int32

@@ -184,9 +184,17 @@ def _dtype_code(dtype) -> int:
     raise _lib.QmmError(-2, "logits must be bfloat16 or float16")
 
 
-def topk(logits: torch.Tensor, k: int, out_index=None, out_value=None):
+def topk_workspace(rows: int, device) -> torch.Tensor:
+    """A zeroed workspace for qmm_topk / qmm_qmv_topk over `rows` rows (reusable in stream
+    order: the kernels leave it zero)."""
+    return torch.zeros((32776 * max(rows, 1) + 7) // 8, dtype=torch.int64, device=device)
+
+
+def topk(logits: torch.Tensor, k: int, out_index=None, out_value=None, workspace=None, split=True):
     """Per-row top-k of a [rows, n] logits tensor (qmm_topk): (index int32 [rows, k], value
-    float32 [rows, k]), largest first, equal values by lower column."""
+    float32 [rows, k]), largest first, equal values by lower column.  With split (default) a
+    workspace lets long rows spread over several workgroups (a fresh one is allocated when
+    `workspace` is None); split=False runs one workgroup per row."""
     lib = _lib.load()
     assert logits.dim() == 2 and logits.stride(1) == 1
     rows, n = logits.shape
@@ -194,14 +202,20 @@ def topk(logits: torch.Tensor, k: int, out_index=None, out_value=None):
     val = out_value if out_value is not None else torch.empty(rows, k, dtype=torch.float32, device=logits.device)
     assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows * k
     assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows * k
+    ws = None
+    if split:
+        ws = workspace if workspace is not None else topk_workspace(rows, logits.device)
+        assert ws.is_contiguous() and ws.numel() * ws.element_size() >= 32776 * rows
     _lib.check(lib.qmm_topk(logits.data_ptr(), _dtype_code(logits.dtype), rows, n, logits.stride(0) if rows else n,
-                            k, idx.data_ptr(), val.data_ptr(), _stream(logits.device)))
+                            k, idx.data_ptr(), val.data_ptr(), ws.data_ptr() if ws is not None else None,
+                            _stream(logits.device)))
     return idx, val
 
 
-def qmv_topk(x: torch.Tensor, qw: QuantizedWeight, k: int, out=None, out_index=None, out_value=None):
+def qmv_topk(x: torch.Tensor, qw: QuantizedWeight, k: int, out=None, out_index=None, out_value=None,
+             workspace=None, split=True):
     """Decode qmv followed by a per-row top-k of its logits (qmm_qmv_topk).  Returns
-    (index int32 [rows, k], value float32 [rows, k], y)."""
+    (index int32 [rows, k], value float32 [rows, k], y); workspace / split as for topk."""
     lib = _lib.load()
     rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
     if out is not None:
@@ -217,8 +231,13 @@ def qmv_topk(x: torch.Tensor, qw: QuantizedWeight, k: int, out=None, out_index=N
         raise _lib.QmmError(-2, "x, scales and biases must share one dtype")
     xd = _lib.tensor_desc(x.shape, x.stride())
     yd = _lib.tensor_desc(y.shape, y.stride())
+    ws = None
+    if split:
+        ws = workspace if workspace is not None else topk_workspace(rows, x.device)
+        assert ws.is_contiguous() and ws.numel() * ws.element_size() >= 32776 * rows
     _lib.check(lib.qmm_qmv_topk(x.data_ptr(), ctypes.byref(xd), ctypes.byref(qw.desc()), y.data_ptr(),
-                                ctypes.byref(yd), k, idx.data_ptr(), val.data_ptr(), _stream(x.device)))
+                                ctypes.byref(yd), k, idx.data_ptr(), val.data_ptr(),
+                                ws.data_ptr() if ws is not None else None, _stream(x.device)))
     return idx, val, y
 
 

@@ -72,22 +72,22 @@ int32_t check_topk(int32_t dtype, int64_t n, int64_t row_stride, int32_t k) {
 extern "C" {
 
 int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int64_t row_stride, int32_t k,
-                 int32_t* out_index, float* out_value, void* stream) {
+                 int32_t* out_index, float* out_value, void* workspace, void* stream) {
   if (rows < 0) return finish(QMM_ERR_SHAPE, "topk: rows must be >= 0");
   const int32_t rc = check_topk(dtype, n, row_stride, k);
   if (rc != QMM_OK) return rc;
   if (rows == 0) return finish(QMM_OK, "");
   if (rows >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "topk: rows must be < 2^31");
   if (!logits || !out_index) return finish(QMM_ERR_NULL, "topk: logits and out_index must be non-NULL");
-  if ((uintptr_t)logits % 2 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
-    return finish(QMM_ERR_ALIGN, "topk: logits must be 2-byte, out_index/out_value 4-byte aligned");
-  const qmm::TopkArgs a{logits, rows, n, row_stride, k, dtype, out_index, out_value};
+  if ((uintptr_t)logits % 2 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4 || (uintptr_t)workspace % 8)
+    return finish(QMM_ERR_ALIGN, "topk: logits must be 2-byte, out_index/out_value 4-byte, workspace 8-byte aligned");
+  const qmm::TopkArgs a{logits, rows, n, row_stride, k, dtype, out_index, out_value, workspace};
   return launch_status(qmm::launch_topk(a, (hipStream_t)stream));
 }
 
 int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                      const qmm_tensor_desc_t* y_desc, int32_t k, int32_t* out_index, float* out_value,
-                     void* stream) {
+                     void* workspace, void* stream) {
   std::string err;
   qmm_plan_t p;
   int rc = qmm::plan_matmul(x, x_desc, w, y, y_desc, 0, 0, true, &p, &err);
@@ -96,13 +96,13 @@ int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_w
   rc = check_topk(w->dtype, w->N, w->N, k);
   if (rc != QMM_OK) return rc;
   if (!out_index) return finish(QMM_ERR_NULL, "qmv_topk: out_index must be non-NULL");
-  if ((uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
-    return finish(QMM_ERR_ALIGN, "qmv_topk: out_index/out_value must be 4-byte aligned");
+  if ((uintptr_t)out_index % 4 || (uintptr_t)out_value % 4 || (uintptr_t)workspace % 8)
+    return finish(QMM_ERR_ALIGN, "qmv_topk: out_index/out_value must be 4-byte, workspace 8-byte aligned");
   const qmm::MatArgs a = make_args(x, p, w, y);
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = p.family == 0 ? qmm::launch_decode(a, s) : qmm::launch_prefill(a, s);
   if (e != hipSuccess) return launch_status(e);
-  const qmm::TopkArgs t{y, p.rows, w->N, w->N, k, w->dtype, out_index, out_value};
+  const qmm::TopkArgs t{y, p.rows, w->N, w->N, k, w->dtype, out_index, out_value, workspace};
   return launch_status(qmm::launch_topk(t, s));
 }
 

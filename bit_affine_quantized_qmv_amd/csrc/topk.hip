@@ -16,8 +16,10 @@
 //   3. the g keys above t go to candidate slots [0, g) in any order; the first k - g keys
 //      equal to t in column order (a block-wide prefix count over consecutive column runs)
 //      go to slots [g, k).
-// The k candidates, as (key << 32 | ~column) words, are sorted in LDS (bitonic) and
-// written out.  The result does not depend on the order in which threads run.
+// The candidates, as (key << 32 | ~column) words, are sorted in LDS (bitonic) and the
+// first k written out.  With a workspace, long rows are cut into column chunks handled by
+// workgroups of their own (enough for about one workgroup per compute unit); the row's
+// last workgroup sorts the chunks' candidates.  The result does not depend on the order in which threads or workgroups run.
 #include <climits>
 
 #include "device_common.hpp"
@@ -87,10 +89,19 @@ __device__ inline void for_each_key(const uint16_t* row, int64_t n, F&& f) {
   for (int64_t i = n8 + threadIdx.x; i < n; i += kThreads) f(i, order_key<FP16>(row[i]));
 }
 
-// Sort the m candidate words cand[0, m) (m <= kCand) descending and store the first k.
-// Padded to a power of two with zero words, which sort below every candidate.
-template <bool FP16>
-__device__ inline void sort_and_store(unsigned long long* cand, uint32_t m, uint32_t k, const TopkArgs& a) {
+// Workgroup-shared state of one selection.
+struct TopkSmem {
+  uint32_t hist[kHiBins];
+  uint32_t wave_sums[kWaves];
+  uint32_t sel[4];
+  uint32_t slot;
+  uint32_t last;
+  unsigned long long cand[kCand];
+};
+
+// Sorts the m words cand[0, m) (m <= kCand) ascending, padded to a power of two mp with
+// zero words (below every candidate), and returns mp: cand[mp - 1 - j] is the j-th largest.
+__device__ inline uint32_t sort_words(unsigned long long* cand, uint32_t m) {
   const uint32_t tid = threadIdx.x;
   uint32_t mp = 1u;
   while (mp < m) mp <<= 1;
@@ -112,86 +123,90 @@ __device__ inline void sort_and_store(unsigned long long* cand, uint32_t m, uint
     }
   }
   __syncthreads();
-  for (uint32_t j = tid; j < k; j += kThreads) {
+  return mp;
+}
+
+// Writes the k largest words (cand sorted by sort_words, mp its padded size) as output row r.
+template <bool FP16>
+__device__ inline void store_words(const unsigned long long* cand, uint32_t mp, uint32_t k, int64_t r,
+                                   const TopkArgs& a) {
+  for (uint32_t j = threadIdx.x; j < k; j += kThreads) {
     const unsigned long long c = cand[mp - 1u - j];
     const uint32_t bits = key_bits((uint32_t)(c >> 32));
-    a.out_index[(int64_t)blockIdx.x * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-    if (a.out_value) a.out_value[(int64_t)blockIdx.x * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
+    a.out_index[r * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+    if (a.out_value) a.out_value[r * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
   }
 }
 
+// The kk largest (key << 32 | ~column) words of columns [col0, col0 + len) of a row, sorted
+// by sort_words; returns the padded size.  `row` points at column col0.
 template <bool FP16>
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
-  __shared__ uint32_t hist[kHiBins];
-  __shared__ uint32_t wave_sums[kWaves];
-  __shared__ uint32_t sel[4];
-  __shared__ uint32_t n_above_slot;
-  __shared__ unsigned long long cand[kCand];
+__device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t col0, int64_t len, uint32_t kk, TopkSmem& sm) {
   const int tid = threadIdx.x;
-  const uint16_t* row = (const uint16_t*)a.logits + (int64_t)blockIdx.x * a.row_stride;
-  const int64_t n = a.n;
-  const uint32_t k = (uint32_t)a.k;
+  const uint32_t k = kk;
+  auto word = [&](uint32_t o, int64_t i) {
+    return ((unsigned long long)o << 32) | (0xFFFFFFFFu - (uint32_t)(col0 + i));
+  };
 
   // 1. histogram of the high bits; the bin of the k-th largest key by a suffix count
-  for (int b = tid; b < kHiBins; b += kThreads) hist[b] = 0u;
+  for (int b = tid; b < kHiBins; b += kThreads) sm.hist[b] = 0u;
   __syncthreads();
-  for_each_key<FP16>(row, n, [&](int64_t, uint32_t o) { atomicAdd(&hist[o >> kHiShift], 1u); });
+  for_each_key<FP16>(row, len, [&](int64_t, uint32_t o) { atomicAdd(&sm.hist[o >> kHiShift], 1u); });
   __syncthreads();
   {
     static_assert(kHiBins == 2 * kThreads, "two bins per thread");
     const int b_hi = kHiBins - 1 - 2 * tid, b_lo = b_hi - 1;   // thread 0 holds the top bins
-    const uint32_t c_hi = hist[b_hi], c_lo = hist[b_lo];
+    const uint32_t c_hi = sm.hist[b_hi], c_lo = sm.hist[b_lo];
     uint32_t total;
-    const uint32_t above = block_exclusive_scan(c_hi + c_lo, wave_sums, &total);
+    const uint32_t above = block_exclusive_scan(c_hi + c_lo, sm.wave_sums, &total);
     if (above < k && above + c_hi >= k) {
-      sel[0] = (uint32_t)b_hi;
-      sel[1] = above;
-      sel[2] = above + c_hi;
+      sm.sel[0] = (uint32_t)b_hi;
+      sm.sel[1] = above;
+      sm.sel[2] = above + c_hi;
     } else if (above + c_hi < k && above + c_hi + c_lo >= k) {
-      sel[0] = (uint32_t)b_lo;
-      sel[1] = above + c_hi;
-      sel[2] = above + c_hi + c_lo;
+      sm.sel[0] = (uint32_t)b_lo;
+      sm.sel[1] = above + c_hi;
+      sm.sel[2] = above + c_hi + c_lo;
     }
-    if (tid == 0) n_above_slot = 0u;
+    if (tid == 0) sm.slot = 0u;
   }
   __syncthreads();
-  const uint32_t hi = sel[0];
-  const uint32_t n_ge = sel[2];   // keys in bin hi or above
+  const uint32_t hi = sm.sel[0];
+  const uint32_t n_ge = sm.sel[2];   // keys in bin hi or above
   if (n_ge <= (uint32_t)kCand) {
     // Usual case: every key in bin hi or above is a candidate (collected in any order; the
-    // sort key carries the column), then sort them all.
-    for_each_key<FP16>(row, n, [&](int64_t i, uint32_t o) {
-      if ((o >> kHiShift) >= hi)
-        cand[atomicAdd(&n_above_slot, 1u)] = ((unsigned long long)o << 32) | (0xFFFFFFFFu - (uint32_t)i);
+    // word carries the column), then sort them all.
+    for_each_key<FP16>(row, len, [&](int64_t i, uint32_t o) {
+      if ((o >> kHiShift) >= hi) sm.cand[atomicAdd(&sm.slot, 1u)] = word(o, i);
     });
-    sort_and_store<FP16>(cand, n_ge, k, a);
-    return;
+    return sort_words(sm.cand, n_ge);
   }
   // Otherwise (a huge tie block at the threshold) find the exact k-th key first.
   // 2. histogram of the low bits inside bin hi
-  if (tid < kLoBins) hist[tid] = 0u;
+  if (tid < kLoBins) sm.hist[tid] = 0u;
   __syncthreads();
-  for_each_key<FP16>(row, n, [&](int64_t, uint32_t o) {
-    if ((o >> kHiShift) == hi) atomicAdd(&hist[o & (kLoBins - 1)], 1u);
+  for_each_key<FP16>(row, len, [&](int64_t, uint32_t o) {
+    if ((o >> kHiShift) == hi) atomicAdd(&sm.hist[o & (kLoBins - 1)], 1u);
   });
   __syncthreads();
   if (tid == 0) {
-    uint32_t above = sel[1];
+    uint32_t above = sm.sel[1];
     int l = kLoBins - 1;
-    for (; l > 0 && above + hist[l] < k; --l) above += hist[l];
-    sel[2] = (hi << kHiShift) | (uint32_t)l;
-    sel[3] = above;
+    for (; l > 0 && above + sm.hist[l] < k; --l) above += sm.hist[l];
+    sm.sel[2] = (hi << kHiShift) | (uint32_t)l;
+    sm.sel[3] = above;
   }
   __syncthreads();
-  const uint32_t t = sel[2], g = sel[3], need_eq = k - g;
+  const uint32_t t = sm.sel[2], g = sm.sel[3], need_eq = k - g;
 
-  // 3. collect
+  // 3. collect: keys above t anywhere in [0, g), the first need_eq keys equal to t in
+  // column order in [g, k)
   const bool vec = ((uintptr_t)row & 15u) == 0u;
   uint32_t eq_seen = 0u;   // keys equal to t in earlier runs (the same in every thread)
-  for (int64_t base = 0; base < n; base += (int64_t)kThreads * kRun) {
+  for (int64_t base = 0; base < len; base += (int64_t)kThreads * kRun) {
     const int64_t i0 = base + (int64_t)tid * kRun;
     uint32_t o[kRun];
-    if (vec && i0 + kRun <= n) {
+    if (vec && i0 + kRun <= len) {
       const u32x4 v = *(const u32x4*)(row + i0);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -201,34 +216,108 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kRun; ++e) o[e] = i0 + e < n ? order_key<FP16>(row[i0 + e]) : 0u;   // real keys are never 0
+      for (int e = 0; e < kRun; ++e) o[e] = i0 + e < len ? order_key<FP16>(row[i0 + e]) : 0u;   // real keys are never 0
     }
     uint32_t neq = 0u;
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
-      if (o[e] > t)
-        cand[atomicAdd(&n_above_slot, 1u)] = ((unsigned long long)o[e] << 32) | (0xFFFFFFFFu - (uint32_t)(i0 + e));
+      if (o[e] > t) sm.cand[atomicAdd(&sm.slot, 1u)] = word(o[e], i0 + e);
       neq += o[e] == t ? 1u : 0u;
     }
     uint32_t total;
-    uint32_t r = eq_seen + block_exclusive_scan(neq, wave_sums, &total);
+    uint32_t r = eq_seen + block_exclusive_scan(neq, sm.wave_sums, &total);
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
       if (o[e] == t) {
-        if (r < need_eq) cand[g + r] = ((unsigned long long)t << 32) | (0xFFFFFFFFu - (uint32_t)(i0 + e));
+        if (r < need_eq) sm.cand[g + r] = word(t, i0 + e);
         ++r;
       }
     }
     eq_seen += total;
   }
-  sort_and_store<FP16>(cand, k, k, a);
+  return sort_words(sm.cand, k);
+}
+
+// One workgroup per row.
+template <bool FP16>
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
+  __shared__ TopkSmem sm;
+  const int64_t r = blockIdx.x;
+  const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride;
+  const uint32_t mp = select_words<FP16>(row, 0, a.n, (uint32_t)a.k, sm);
+  store_words<FP16>(sm.cand, mp, (uint32_t)a.k, r, a);
+}
+
+// Rows cut into `parts` column chunks of `chunk` columns (a multiple of 8), one workgroup
+// per (chunk, row).  Each writes its chunk's k largest words (zero words past a short
+// chunk) to the workspace, then counts itself done on the row's counter; the row's last
+// workgroup sorts the parts * k words (at most kCand) and writes the row's result, then
+// clears the counter.  Candidate words travel through device-scope atomic stores and loads;
+// each writer waits for its stores to complete before its workgroup is counted.
+template <bool FP16>
+__global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, const int parts, const int64_t chunk) {
+  __shared__ TopkSmem sm;
+  const int c = blockIdx.x;
+  const int64_t r = blockIdx.y;
+  const uint32_t k = (uint32_t)a.k;
+  const int64_t col0 = (int64_t)c * chunk;
+  const int64_t len = a.n - col0 < chunk ? a.n - col0 : chunk;
+  const uint32_t kk = (int64_t)k < len ? k : (uint32_t)len;
+  const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride + col0;
+  const uint32_t mp = select_words<FP16>(row, col0, len, kk, sm);
+  unsigned int* counters = (unsigned int*)a.workspace;
+  unsigned long long* words = (unsigned long long*)a.workspace + kTopkWsHeader * a.rows + (r * parts + c) * (int64_t)k;
+  for (uint32_t j = threadIdx.x; j < k; j += kThreads)
+    __hip_atomic_store(&words[j], j < kk ? sm.cand[mp - 1u - j] : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The words are device-scope atomic stores; once this thread's stores have completed
+  // (vmcnt 0) they are visible device-wide, before the workgroup counts itself done.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned done = __hip_atomic_fetch_add(&counters[2 * r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = done + 1u == (unsigned)parts ? 1u : 0u;
+  }
+  __syncthreads();
+  if (sm.last == 0u) return;
+  const unsigned long long* row_words = (const unsigned long long*)a.workspace + kTopkWsHeader * a.rows + r * parts * (int64_t)k;
+  const uint32_t m = (uint32_t)parts * k;
+  for (uint32_t j = threadIdx.x; j < m; j += kThreads)
+    sm.cand[j] = __hip_atomic_load(&row_words[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t mp2 = sort_words(sm.cand, m);
+  store_words<FP16>(sm.cand, mp2, k, r, a);
+  if (threadIdx.x == 0) __hip_atomic_store(&counters[2 * r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
+// Columns per part: enough parts for about one workgroup per compute unit over all rows,
+// parts of at least 4096 columns, and parts * k within what one workgroup sorts.
+int64_t topk_chunk(int64_t n, int k, int64_t rows, int* parts) {
+  int64_t p = (256 + rows - 1) / rows;
+  const int64_t p_cols = (n + 4095) / 4096;
+  if (p > p_cols) p = p_cols;
+  const int64_t p_max = kCand / k;
+  if (p > p_max) p = p_max;
+  if (p < 1) p = 1;
+  int64_t chunk = (n + p - 1) / p;
+  chunk = (chunk + 7) / 8 * 8;   // 16-byte aligned chunk starts
+  *parts = (int)((n + chunk - 1) / chunk);
+  return chunk;
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   if (a.k < 1 || a.k > kTopkMax || a.k > a.n || a.rows > INT_MAX) return hipErrorInvalidValue;
+  int parts = 1;
+  const int64_t chunk = topk_chunk(a.n, a.k, a.rows, &parts);
+  if (a.workspace && parts > 1 && a.rows <= 65535) {
+    const dim3 grid((unsigned)parts, (unsigned)a.rows);
+    if (a.dtype == 2)
+      hipLaunchKernelGGL((topk_parts_kernel<true>), grid, dim3(kThreads), 0, stream, a, parts, chunk);
+    else
+      hipLaunchKernelGGL((topk_parts_kernel<false>), grid, dim3(kThreads), 0, stream, a, parts, chunk);
+    return hipGetLastError();
+  }
   if (a.dtype == 2)
     hipLaunchKernelGGL((topk_rows_kernel<true>), dim3((unsigned)a.rows), dim3(kThreads), 0, stream, a);
   else

@@ -9,6 +9,10 @@ namespace qmm {
 
 // Largest k the top-k kernel takes.
 constexpr int kTopkMax = 1024;
+// Workspace layout: per row a counter word pair (8 bytes), then per row 4096 candidate
+// words (8 bytes each): 8 + 32768 bytes per row.
+constexpr int64_t kTopkWsHeader = 1;        // 8-byte words of counters per row
+constexpr int64_t kTopkWsRowWords = 4096;   // candidate words per row
 
 struct TopkArgs {
   const void* logits;   // [rows, row_stride] of dtype (1 = bf16, 2 = fp16)
@@ -19,6 +23,7 @@ struct TopkArgs {
   int32_t dtype;
   int32_t* out_index;   // [rows, k]
   float* out_value;     // [rows, k] or null
+  void* workspace;      // null (one workgroup per row) or the row-split workspace
 };
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);

@@ -203,18 +203,26 @@ int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
  * row_stride >= n.  out_index: DEVICE int32 [rows, k], 4-byte aligned; out_value: DEVICE
  * float32 [rows, k] or NULL.  Need 0 < n < 2^31, 0 <= rows < 2^31 and
  * 1 <= k <= min(n, QMM_TOPK_MAX) (QMM_ERR_SHAPE otherwise); rows == 0 is a no-op.
- * One kernel is enqueued (a workgroup per row); nothing is allocated. */
+ * workspace: NULL, or DEVICE, 8-byte aligned, QMM_TOPK_WORKSPACE_BYTES(rows) bytes that are
+ * ALL ZERO when the call's kernel starts (zero-fill once when allocated; the kernel leaves
+ * the counters it uses zero again, so one workspace serves any number of calls in stream
+ * order; calls that may overlap need workspaces of their own).  With a workspace, long rows
+ * are split over several workgroups (column chunks of at least 4096, about one workgroup
+ * per compute unit in all); without one, each row is one workgroup.  The results are the
+ * same either way.
+ * One kernel is enqueued; nothing is allocated. */
 #define QMM_TOPK_MAX 1024
+#define QMM_TOPK_WORKSPACE_BYTES(rows) (32776 * (rows))
 int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int64_t row_stride, int32_t k,
-                 int32_t* out_index, float* out_value, void* stream);
+                 int32_t* out_index, float* out_value, void* workspace, void* stream);
 
 /* Decode with a per-row top-k: y = x . dequant(W)^T exactly as qmv (y is required and
  * dense, contract as for qmv), then qmm_topk over the rows of y (n = N, row_stride = N)
- * into out_index / out_value [rows, k].  k is checked before anything is enqueued.
- * Two kernels are enqueued. */
+ * into out_index / out_value [rows, k], with `workspace` as for qmm_topk.  k is checked
+ * before anything is enqueued.  Two kernels are enqueued. */
 int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                      const qmm_tensor_desc_t* y_desc, int32_t k, int32_t* out_index, float* out_value,
-                     void* stream);
+                     void* workspace, void* stream);
 
 /* Dequantize a whole quantized weight to a dense matrix: out[n, k] = RNE_dtype(fl32(fma(s, q, b)))
  * with s, b the (n, k / group_size) scale and bias and q the code (transformers issue 47331,

@@ -31,9 +31,10 @@ def test_topk_random_rows(rows, n, k, dtype):
     import bit_affine_quantized_qmv_amd as q
     dev = require_gpu()
     logits = synth.normal_x((rows, n), dtype, seed=1000 + n + k).to(dev)
-    idx, val = q.topk(logits, k)
-    torch.cuda.synchronize()
-    _check(logits, idx, val, k, dtype)
+    for split in (True, False):   # rows over several workgroups, and one workgroup per row
+        idx, val = q.topk(logits, k, split=split)
+        torch.cuda.synchronize()
+        _check(logits, idx, val, k, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -125,6 +126,36 @@ def test_topk_huge_tie_blocks(levels, k, dtype):
     import bit_affine_quantized_qmv_amd as q
     dev = require_gpu()
     logits = synth.tied_logits(3, 20011, levels, dtype, seed=1600 + levels).to(dev)
-    idx, val = q.topk(logits, k)
+    for split in (True, False):
+        idx, val = q.topk(logits, k, split=split)
+        torch.cuda.synchronize()
+        _check(logits, idx, val, k, dtype)
+
+
+def test_topk_workspace_reuse_and_graph_replay():
+    # the row-split kernel leaves its counters zero: one workspace serves calls in stream
+    # order, eager and replayed from a graph
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    rows, n, k = 5, 50001, 77
+    ws = q.topk_workspace(rows, dev)
+    srcs = [synth.normal_x((rows, n), "bf16", seed=1700 + i).to(dev) for i in range(3)]
+    for lg in srcs:
+        idx, val = q.topk(lg, k, workspace=ws)
+        torch.cuda.synchronize()
+        _check(lg, idx, val, k, "bf16")
+    buf = srcs[0].clone()
+    idx = torch.empty(rows, k, dtype=torch.int32, device=dev)
+    val = torch.empty(rows, k, dtype=torch.float32, device=dev)
+    q.topk(buf, k, out_index=idx, out_value=val, workspace=ws)   # warm up outside the capture
     torch.cuda.synchronize()
-    _check(logits, idx, val, k, dtype)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.topk(buf, k, out_index=idx, out_value=val, workspace=ws)
+    for lg in srcs[::-1]:
+        buf.copy_(lg)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _check(lg, idx, val, k, "bf16")
+    assert int(ws.abs().sum()) >= 0 and int(ws.view(torch.int32)[: 2 * rows].abs().sum()) == 0
