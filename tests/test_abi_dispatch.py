@@ -178,13 +178,13 @@ def test_topk_validation_before_any_launch():
     # every rejection happens on the host, before anything is enqueued (no GPU needed)
     lib = q.load()
     codes = {name: code for code, name in _lib.ERRORS.items()}
-    assert lib.qmm_topk(None, 1, 4, 10, 10, 0, None, None, None) == codes["QMM_ERR_SHAPE"]
-    assert lib.qmm_topk(None, 1, 4, 10, 10, 11, None, None, None) == codes["QMM_ERR_SHAPE"]
-    assert lib.qmm_topk(None, 1, 4, 2000, 2000, 1025, None, None, None) == codes["QMM_ERR_SHAPE"]
-    assert lib.qmm_topk(None, 1, 4, 10, 9, 3, None, None, None) == codes["QMM_ERR_SHAPE"]
-    assert lib.qmm_topk(None, 1, -1, 10, 10, 3, None, None, None) == codes["QMM_ERR_SHAPE"]
-    assert lib.qmm_topk(None, 3, 4, 10, 10, 3, None, None, None) == codes["QMM_ERR_UNSUPPORTED"]
+    assert lib.qmm_topk(None, 1, 4, 10, 10, 0, None, None, None, None) == codes["QMM_ERR_SHAPE"]
+    assert lib.qmm_topk(None, 1, 4, 10, 10, 11, None, None, None, None) == codes["QMM_ERR_SHAPE"]
+    assert lib.qmm_topk(None, 1, 4, 2000, 2000, 1025, None, None, None, None) == codes["QMM_ERR_SHAPE"]
+    assert lib.qmm_topk(None, 1, 4, 10, 9, 3, None, None, None, None) == codes["QMM_ERR_SHAPE"]
+    assert lib.qmm_topk(None, 1, -1, 10, 10, 3, None, None, None, None) == codes["QMM_ERR_SHAPE"]
+    assert lib.qmm_topk(None, 3, 4, 10, 10, 3, None, None, None, None) == codes["QMM_ERR_UNSUPPORTED"]
     assert b"dtype" in lib.qmm_last_error()
-    assert lib.qmm_topk(None, 1, 4, 10, 10, 3, None, None, None) == codes["QMM_ERR_NULL"]
-    assert lib.qmm_topk(None, 2, 0, 10, 10, 3, None, None, None) == 0   # no rows: a no-op
+    assert lib.qmm_topk(None, 1, 4, 10, 10, 3, None, None, None, None) == codes["QMM_ERR_NULL"]
+    assert lib.qmm_topk(None, 2, 0, 10, 10, 3, None, None, None, None) == 0   # no rows: a no-op
     assert lib.qmm_last_error() == b""
