@@ -58,6 +58,22 @@ def _traffic(summary_name, kernel_sources):
     return None
 
 
+def _profile_field(summary_name, tag, kernel_sources, field):
+    """One value from a committed rocprofv3 --pmc summary (a line '<tag>: {...}' in
+    profiles/<summary_name>), if its counters were taken on the current kernel source."""
+    path = os.path.join(PROFILES, summary_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith(tag + ":"):
+                d = json.loads(ln.split(":", 1)[1])
+                if d.get("source_hash") != _source_hash(kernel_sources):
+                    return None
+                return d.get(field)
+    return None
+
+
 def _time_steps(fn, steps, warmup, torch, use_graph=True):
     """Times `steps` calls of fn(i) three ways:
 
@@ -429,7 +445,10 @@ def main():
                          "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": _traffic("qmm_prefill_dma_kernel_prefill_traffic.md", QMM_T_SOURCES),
                          "kernel": "qmm_prefill_dma_kernel", "kernel_ms_mean": round(pt["kernel_mean_ms"], 5),
-                         "kernel_ms_median": round(pt["kernel_median_ms"], 5)},
+                         "kernel_ms_median": round(pt["kernel_median_ms"], 5),
+                         # matrix-core busy fraction from the SQ_VALU_MFMA_BUSY_CYCLES counter
+                         "mfma_util_counter": _profile_field("qmm_prefill_dma_kernel_prefill_mfma_util.md",
+                                                             "mfma-util-json", QMM_T_SOURCES, "mfma_util")},
         }
         del pqs, pxs, pys, buf, pw
 

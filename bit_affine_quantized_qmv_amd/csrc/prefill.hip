@@ -175,9 +175,9 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs 
       }
 }
 
-// Source of the activation chunks that lie past the call's rows or past K: the direct
-// global-to-LDS loads cannot zero a lane, so such lanes read this zero chunk instead.
-__device__ const u32x4 kZeroChunk = {0u, 0u, 0u, 0u};
+// Bytes the activation descriptor of the direct-load kernel spans from a batch's first
+// row; the launcher checks that the rows it reads lie inside.
+constexpr uint32_t kXRange = 0x7FFFFF00u;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -220,29 +220,35 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_dma_kernel(const MatA
 
   // activation loads: load j of this wave covers tile rows r0 = 8 * (4 * wave + j) .. r0 + 7;
   // lane i fills position i % 8 of row r0 + i / 8, i.e. logical chunk (i % 8) ^ ((r >> 1) & 7)
-  const uint16_t* asrc[A_LOADS];
+  // Byte offsets into the batch's activations (a descriptor of 2 GiB, which the host checks
+  // the rows fit in); lanes past the call's rows or past K get an offset past the
+  // descriptor's end and so read zeros.
+  const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xb), (short)0,
+                                                                       (int)kXRange, 0x00020000);
+  constexpr uint32_t kPast = kXRange;   // at or past the end: the whole chunk reads zero
+  uint32_t aoff[A_LOADS];
   int ak[A_LOADS];
-  bool arow_ok[A_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
     const int r = 8 * (A_LOADS * wave + j) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int64_t m = bm0 + r;
-    arow_ok[j] = m < rows;
     const int64_t mr = m < rows ? m : 0;
     ak[j] = 8 * c;
-    asrc[j] = xb + (mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride + 8 * c;
+    aoff[j] = m < rows ? (uint32_t)(2 * ((mr / a.seg_rows) * a.seg_stride + (mr % a.seg_rows) * a.row_stride + 8 * c))
+                       : kPast;
   }
   // When K is not a multiple of BK the last step is partial: activation chunks at k >= K
-  // read the zero chunk, and code runs at k >= K read the row's first run and are zeroed (K
-  // is a multiple of 32, so a chunk or run is either wholly inside or wholly outside the row).
+  // read zeros, and code runs at k >= K read the row's first run and are zeroed (K is a
+  // multiple of 32, so a chunk or run is either wholly inside or wholly outside the row).
+  uint32_t aoff_k[A_LOADS];   // this step's offsets, kept allocated until the step's wait
   auto load_a = [&](int kt, u32x4* dst) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-      const bool ok = arow_ok[j] && k0 + ak[j] < K;
-      const void* src = ok ? (const void*)(asrc[j] + k0) : (const void*)&kZeroChunk;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + 64 * (A_LOADS * wave + j)), 16, 0, 0);
+      aoff_k[j] = (k0 + ak[j] < K && aoff[j] != kPast) ? aoff[j] + 2u * (uint32_t)k0 : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void_t*)(dst + 64 * (A_LOADS * wave + j)), 16, aoff_k[j], 0,
+                                               0, 0);
     }
   };
   // weight: thread -> row wr, 32-code half wh of the 64 k of a step
@@ -325,8 +331,22 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_dma_kernel(const MatA
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = T::mfma(av[i], bv[j], acc[i][j]);
-    // vmcnt(0): the direct activation loads of step kt+1 (and the weights of step kt+2)
+    // vmcnt(0): the direct activation loads of step kt+1 (and the weights of step kt+2).
+    // Their offset registers stay allocated until here: the compiler counts a direct load
+    // as writing its offset register, so a value placed in that register while the load is
+    // in flight would make it wait for the load there.
+    // The accumulators pass through empty statements first, so that the step's MFMAs are
+    // not moved below the wait.  (The fp16 instantiation keeps the compiler's order: with
+    // the pin it no longer fits 256 registers.)
+    if constexpr (T::kDtype == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) asm volatile("" ::"v"(aoff_k[j]));
     load_w(kt + 3, rw, rs, rb);
     lds_barrier();
   };
@@ -372,12 +392,20 @@ hipError_t launch_bits(const MatArgs& a, hipStream_t stream) {
   const int64_t n_tiles = (a.N + BN - 1) / BN;
   if (m_tiles * n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(m_tiles * n_tiles), 1, (unsigned)a.batches);
-  // 4-bit codes take the kernel with direct activation loads; at the other widths its
-  // register budget (256 per lane at two waves per SIMD) does not hold without spills
-  if constexpr (BITS == 4)
-    hipLaunchKernelGGL((qmm_prefill_dma_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
-  else
-    hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
+  // 4-bit codes take the kernel with direct activation loads (when a batch's activations
+  // fit its descriptor); at the other widths its register budget (256 per lane at two
+  // waves per SIMD) does not hold without spills
+  // activation elements a batch spans (rows through the plan's row addressing, plus K)
+  const int64_t rpb = a.rows_per_batch;
+  const int64_t seg_rows_used = rpb < a.seg_rows ? rpb : a.seg_rows;
+  const int64_t span = (rpb - 1) / a.seg_rows * a.seg_stride + (seg_rows_used - 1) * a.row_stride + a.K;
+  if constexpr (BITS == 4) {
+    if (2 * span <= (int64_t)kXRange) {
+      hipLaunchKernelGGL((qmm_prefill_dma_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((qmm_prefill_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
   return hipGetLastError();
 }
 
