@@ -9,9 +9,9 @@
 // row of every batch element must be computed).
 //
 // Two kernels share this arithmetic and the 256 x 256 x 64 tiling.  qmm_prefill_kernel
-// stages the activation tile through registers.  qmm_prefill_dma_kernel (4-bit codes)
-// moves it with direct global-to-LDS loads a whole step ahead, and keeps the weight codes
-// of two steps in registers, so both loads have a full step of MFMAs to land behind.
+// stages the activation tile through registers.  qmm_prefill_dma_kernel (2-, 4- and 8-bit
+// codes) moves it with direct global-to-LDS loads a whole step ahead, and keeps the weight
+// codes of two steps in registers, so both loads have a full step of MFMAs to land behind.
 #include "dequant_impl.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -392,14 +392,14 @@ hipError_t launch_bits(const MatArgs& a, hipStream_t stream) {
   const int64_t n_tiles = (a.N + BN - 1) / BN;
   if (m_tiles * n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(m_tiles * n_tiles), 1, (unsigned)a.batches);
-  // 4-bit codes take the kernel with direct activation loads (when a batch's activations
-  // fit its descriptor); at the other widths its register budget (256 per lane at two
-  // waves per SIMD) does not hold without spills
+  // 2-, 4- and 8-bit codes take the kernel with direct activation loads (when a batch's
+  // activations fit its descriptor); at 3, 5 and 6 bits its register budget (256 per lane
+  // at two waves per SIMD) does not hold without spills
   // activation elements a batch spans (rows through the plan's row addressing, plus K)
   const int64_t rpb = a.rows_per_batch;
   const int64_t seg_rows_used = rpb < a.seg_rows ? rpb : a.seg_rows;
   const int64_t span = (rpb - 1) / a.seg_rows * a.seg_stride + (seg_rows_used - 1) * a.row_stride + a.K;
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
     if (2 * span <= (int64_t)kXRange) {
       hipLaunchKernelGGL((qmm_prefill_dma_kernel<T, BITS>), grid, dim3(kThreads), 0, stream, a, (int)m_tiles);
       return hipGetLastError();
