@@ -126,20 +126,37 @@ __device__ inline uint32_t sort_words(unsigned long long* cand, uint32_t m) {
   return mp;
 }
 
-// Writes the k largest words (cand sorted by sort_words, mp its padded size) as output row r.
+// Writes word w as entry j of output row r.
 template <bool FP16>
-__device__ inline void store_words(const unsigned long long* cand, uint32_t mp, uint32_t k, int64_t r,
-                                   const TopkArgs& a) {
-  for (uint32_t j = threadIdx.x; j < k; j += kThreads) {
-    const unsigned long long c = cand[mp - 1u - j];
-    const uint32_t bits = key_bits((uint32_t)(c >> 32));
-    a.out_index[r * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-    if (a.out_value) a.out_value[r * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
-  }
+__device__ inline void store_word(unsigned long long w, uint32_t j, uint32_t k, int64_t r, const TopkArgs& a) {
+  const uint32_t bits = key_bits((uint32_t)(w >> 32));
+  a.out_index[r * k + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)w);
+  if (a.out_value) a.out_value[r * k + j] = FP16 ? Fp16::to_f32(bits) : Bf16::to_f32(bits);
 }
 
-// The kk largest (key << 32 | ~column) words of columns [col0, col0 + len) of a row, sorted
-// by sort_words; returns the padded size.  `row` points at column col0.
+// Calls f(j, word) for the j-th largest of the m distinct words cand[0, m), j < kk.  Up to
+// 512 words each thread ranks one word by counting the larger ones (no barriers); beyond
+// that the words are sorted.
+constexpr uint32_t kRankMax = 512;
+template <class F>
+__device__ inline void emit_largest(unsigned long long* cand, uint32_t m, uint32_t kk, F&& f) {
+  if (m <= kRankMax) {
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < m; i += kThreads) {
+      const unsigned long long w = cand[i];
+      uint32_t r = 0u;
+      for (uint32_t j = 0; j < m; ++j) r += cand[j] > w ? 1u : 0u;
+      if (r < kk) f(r, w);
+    }
+    return;
+  }
+  const uint32_t mp = sort_words(cand, m);
+  for (uint32_t j = threadIdx.x; j < kk; j += kThreads) f(j, cand[mp - 1u - j]);
+}
+
+// Collects candidate (key << 32 | ~column) words of columns [col0, col0 + len) of a row into
+// cand and returns their number m >= kk; the kk largest of them are the kk largest of the
+// columns.  `row` points at column col0.
 template <bool FP16>
 __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t col0, int64_t len, uint32_t kk, TopkSmem& sm) {
   const int tid = threadIdx.x;
@@ -179,7 +196,7 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
     for_each_key<FP16>(row, len, [&](int64_t i, uint32_t o) {
       if ((o >> kHiShift) >= hi) sm.cand[atomicAdd(&sm.slot, 1u)] = word(o, i);
     });
-    return sort_words(sm.cand, n_ge);
+    return n_ge;
   }
   // Otherwise (a huge tie block at the threshold) find the exact k-th key first.
   // 2. histogram of the low bits inside bin hi
@@ -235,7 +252,7 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
     }
     eq_seen += total;
   }
-  return sort_words(sm.cand, k);
+  return k;
 }
 
 // One workgroup per row.
@@ -244,8 +261,9 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
   __shared__ TopkSmem sm;
   const int64_t r = blockIdx.x;
   const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride;
-  const uint32_t mp = select_words<FP16>(row, 0, a.n, (uint32_t)a.k, sm);
-  store_words<FP16>(sm.cand, mp, (uint32_t)a.k, r, a);
+  const uint32_t k = (uint32_t)a.k;
+  const uint32_t m = select_words<FP16>(row, 0, a.n, k, sm);
+  emit_largest(sm.cand, m, k, [&](uint32_t j, unsigned long long w) { store_word<FP16>(w, j, k, r, a); });
 }
 
 // Rows cut into `parts` column chunks of `chunk` columns (a multiple of 8), one workgroup
@@ -264,11 +282,14 @@ __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, 
   const int64_t len = a.n - col0 < chunk ? a.n - col0 : chunk;
   const uint32_t kk = (int64_t)k < len ? k : (uint32_t)len;
   const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride + col0;
-  const uint32_t mp = select_words<FP16>(row, col0, len, kk, sm);
+  const uint32_t mc = select_words<FP16>(row, col0, len, kk, sm);
   unsigned int* counters = (unsigned int*)a.workspace;
   unsigned long long* words = (unsigned long long*)a.workspace + kTopkWsHeader * a.rows + (r * parts + c) * (int64_t)k;
-  for (uint32_t j = threadIdx.x; j < k; j += kThreads)
-    __hip_atomic_store(&words[j], j < kk ? sm.cand[mp - 1u - j] : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  emit_largest(sm.cand, mc, kk, [&](uint32_t j, unsigned long long w) {
+    __hip_atomic_store(&words[j], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+  for (uint32_t j = kk + threadIdx.x; j < k; j += kThreads)   // a chunk shorter than k
+    __hip_atomic_store(&words[j], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The words are device-scope atomic stores; once this thread's stores have completed
   // (vmcnt 0) they are visible device-wide, before the workgroup counts itself done.
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -283,8 +304,7 @@ __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, 
   const uint32_t m = (uint32_t)parts * k;
   for (uint32_t j = threadIdx.x; j < m; j += kThreads)
     sm.cand[j] = __hip_atomic_load(&row_words[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t mp2 = sort_words(sm.cand, m);
-  store_words<FP16>(sm.cand, mp2, k, r, a);
+  emit_largest(sm.cand, m, k, [&](uint32_t j, unsigned long long w) { store_word<FP16>(w, j, k, r, a); });
   if (threadIdx.x == 0) __hip_atomic_store(&counters[2 * r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
