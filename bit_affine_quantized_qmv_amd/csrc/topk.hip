@@ -5,21 +5,23 @@
 // to token 0; keeping per-row candidates instead of whole logit rows is what a sharded
 // lm_head exchanges).
 //
-// One 1024-thread workgroup per row, three passes over the row's 16-bit values mapped to
-// order keys (unsigned, larger key = larger value), read 8 at a time when the row is
-// 16-byte aligned:
+// A 1024-thread workgroup per row (or per column chunk of a row), over the row's 16-bit
+// values mapped to order keys (unsigned, larger key = larger value), read 8 at a time when
+// the row is 16-byte aligned:
 //   1. histogram of the key's high 11 bits (2048 bins, so that the values of a typical
 //      logit row spread over many LDS counters) -> the bin that holds the k-th largest key,
 //      found with a block-wide suffix count;
-//   2. histogram of the low 5 bits inside that bin -> the k-th largest key itself (t) and
-//      the number of keys above it (g < k);
-//   3. the g keys above t go to candidate slots [0, g) in any order; the first k - g keys
-//      equal to t in column order (a block-wide prefix count over consecutive column runs)
-//      go to slots [g, k).
-// The candidates, as (key << 32 | ~column) words, are sorted in LDS (bitonic) and the
-// first k written out.  With a workspace, long rows are cut into column chunks handled by
-// workgroups of their own (enough for about one workgroup per compute unit); the row's
-// last workgroup sorts the chunks' candidates.  The result does not depend on the order in which threads or workgroups run.
+//   2. usual case, at most 4096 keys in that bin and above: all of them are the candidates;
+//   3. otherwise, a histogram of the low 5 bits inside that bin gives the k-th largest key
+//      itself (t) and the number of keys above it (g < k); the g keys above t are the
+//      candidates [0, g) in any order, and the first k - g keys equal to t in column order
+//      (a block-wide prefix count over consecutive column runs) are [g, k).
+// The candidates, as (key << 32 | ~column) words, are ranked: up to 512 by counting the
+// larger words, more by a bitonic sort in LDS; the first k are written out.  With a
+// workspace, long rows are cut into column chunks handled by workgroups of their own
+// (enough for about one workgroup per compute unit); the row's last workgroup ranks the
+// chunks' candidates.  The result does not depend on the order in which threads or
+// workgroups run.
 #include <climits>
 
 #include "device_common.hpp"
