@@ -26,7 +26,7 @@ def _check(logits, idx, val, k, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("rows,n,k", [(1, 1, 1), (3, 100, 7), (5, 1000, 64), (2, 4099, 1024), (4, 20000, 50),
-                                      (7, 333, 333), (2, 65537, 3)])
+                                      (7, 333, 333), (2, 65537, 3), (1, 151936, 50), (1, 151936, 1)])
 def test_topk_random_rows(rows, n, k, dtype):
     import bit_affine_quantized_qmv_amd as q
     dev = require_gpu()
