@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_dma_kernel(const MatA
   lds_barrier();
   // Steps run in pairs, so that every register set and buffer is named statically; an odd
   // step count gets one more step whose operands are all zero (activations past K read the
-  // zero chunk, weights past K have zero scale and bias), which adds nothing.
+  // zeros through the descriptor, weights past K have zero scale and bias), which adds nothing.
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, As0, As1, Bs0, Bs1, rwB, rsB, rbB);
     step(kt + 1, As1, As0, Bs1, Bs0, rwA, rsA, rbA);
