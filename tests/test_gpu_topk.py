@@ -159,3 +159,32 @@ def test_topk_workspace_reuse_and_graph_replay():
         torch.cuda.synchronize()
         _check(lg, idx, val, k, "bf16")
     assert int(ws.abs().sum()) >= 0 and int(ws.view(torch.int32)[: 2 * rows].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("dtype,bits,gs", [("fp16", 8, 32), ("bf16", 4, 128), ("fp16", 3, 64)])
+def test_qmv_topk_small_and_graph(dtype, bits, gs):
+    # decode + top-k on a small weight, eager and replayed from a graph: y equals qmv's, the
+    # indices and values equal the oracle's top-k of that y
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    n, kd, k = 20033, 256, 40
+    w = synth.normal_weight(n, kd, 0.02, seed=1800 + bits).to(dev)
+    qw = q.quantize(w, gs, bits, dtype)
+    x = synth.normal_x((5, 1, kd), dtype, seed=1801).to(dev)
+    ws = q.topk_workspace(5, dev)
+    idx, val, y = q.qmv_topk(x, qw, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), q.qmv(x, qw).view(torch.int16))
+    _check(y.view(5, n), idx, val, k, dtype)
+    yb = torch.empty_like(y)
+    ib = torch.empty_like(idx)
+    vb = torch.empty_like(val)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qmv_topk(x, qw, k, out=yb, out_index=ib, out_value=vb, workspace=ws)
+    for _ in range(3):
+        ib.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ib, idx) and torch.equal(vb, val)
