@@ -79,9 +79,10 @@ def _time_steps(fn, steps, warmup, torch, use_graph=True):
 
     wall_ms    -- the steps captured once into a HIP graph, whose replay is bracketed by
                   torch.cuda.synchronize() on both sides (host wall clock per step);
-    kernel_ms  -- the same steps launched eagerly behind a sleep kernel, so the queue stays
-                  ahead of the host, with an event pair around every launch on the launch
-                  stream (mean / median / p10 / p90 of the per-launch durations);
+    kernel_ms  -- the same steps launched eagerly behind untimed launches of the same step,
+                  so the queue stays ahead of the host, with an event pair around every
+                  launch on the launch stream (mean / median / p10 / p90 of the per-launch
+                  durations);
     eager_ms   -- the steps launched eagerly from Python with synchronize on both sides
                   (includes the host's per-call marshalling; context only).
     """
@@ -120,18 +121,16 @@ def _time_steps(fn, steps, warmup, torch, use_graph=True):
         graph_ok = False
         wall_ms = eager_ms
 
-    # queue primed with a sleep kernel long enough to cover the host's enqueue time
+    # The queue is primed with untimed launches of the same step, enough GPU work to cover
+    # the host's enqueue time of the timed launches, so those run back to back at the
+    # clock the device holds under this load.  (A spin kernel as the primer lets the clock
+    # drop: the prefill kernel then averaged ~270 us instead of ~225 us.)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    torch.cuda._sleep(1_000_000)
-    b.record()
-    torch.cuda.synchronize()
-    cycles_per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
     host_ms = 3.0 * eager_ms * steps + 5.0
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda._sleep(int(cycles_per_ms * host_ms))
+    for i in range(int(host_ms / max(min(wall_ms, eager_ms), 1e-3)) + 1):
+        fn(i)
     for i in range(steps):
         starts[i].record()
         fn(i)
