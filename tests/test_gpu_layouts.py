@@ -1,0 +1,121 @@
+"""GPU parity for activation layouts the dispatcher accepts but the workload tests do not
+reach: broadcast (stride-0) batch dims in decode and prefill, every batch element checked
+against the oracle (candle pitfall page "Metal 上批量 matmul 结果不对", section 怎么确认没中招:
+check every batch element, not only the first), the quick-reproduction shape of MLX pull
+request 4516 ("Validation and quick reproduction": K = 2560, one output feature, 8-bit
+codes, group 64), and run-to-run determinism on every decode kernel path."""
+import pytest
+import torch
+
+import oracle as O
+import synth
+from qmm_testlib import assert_close, gather, reference_rows, require_gpu, values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _quantized(q, dev, n, k, gs, bits, dtype, seed, std=1.0):
+    return q.quantize(synth.normal_weight(n, k, std, seed=seed).to(dev), gs, bits, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("bits", [4, 8, 3])
+def test_broadcast_rows_decode(dev, dtype, bits):
+    """x.expand over a batch dim (stride 0): one level of 8 identical rows, and two levels
+    [4, 3, K] with batch stride 0.  Every row within the bound (the oracle gathers the rows
+    from the base storage through the view's strides) and equal, bit for bit, to the call
+    on the base row alone."""
+    import bit_affine_quantized_qmv_amd as q
+    n, k, gs = 300, 512, 64
+    qw = _quantized(q, dev, n, k, gs, bits, dtype, seed=60 + bits)
+    base = synth.normal_x((1, k), dtype, seed=61).to(dev)
+    x1 = base.expand(8, k)
+    assert x1.stride() == (0, 1)
+    y1 = q.qmv(x1, qw)
+    assert_close(y1, reference_rows(gather(base, x1), qw, dtype), "expand 8")
+    y_base = q.qmv(base, qw)
+    for r in range(8):
+        assert torch.equal(y1[r], y_base[0]), r
+    base3 = synth.normal_x((1, 3, k), dtype, seed=62).to(dev)
+    x2 = base3.expand(4, 3, k)
+    assert x2.stride() == (0, k, 1)
+    y2 = q.qmv(x2, qw)
+    assert y2.shape == (4, 3, n)
+    assert_close(y2.reshape(12, n), reference_rows(gather(base3, x2), qw, dtype), "expand 4x3")
+    y_b3 = q.qmv(base3[0], qw)
+    for b in range(4):
+        assert torch.equal(y2[b], y_b3), b
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_broadcast_rows_prefill(dev, dtype):
+    """Prefill with a stride-0 batch dim: x = base.expand(4, 160, K) (640 rows through the
+    MFMA kernel).  Every row within the bound, each batch element equal to the call on the
+    base rows, bit for bit."""
+    import bit_affine_quantized_qmv_amd as q
+    n, k, gs = 264, 768, 128
+    qw = _quantized(q, dev, n, k, gs, 4, dtype, seed=63)
+    base = synth.normal_x((1, 160, k), dtype, seed=64).to(dev)
+    x = base.expand(4, 160, k)
+    assert x.stride() == (0, k, 1)
+    y = q.qmm_t(x, qw)
+    assert_close(y.reshape(640, n), reference_rows(gather(base, x), qw, dtype), "prefill expand")
+    y_base = q.qmm_t(base[0], qw)
+    for b in range(4):
+        assert torch.equal(y[b], y_base), b
+
+
+@pytest.mark.parametrize("rows", [1, 4, 32])
+def test_pr_reproduction_shape(dev, rows):
+    """K = 2560, N = 1, 8-bit codes, group 64, bf16 (the pull request's quick reproduction):
+    within the bound, and row i of the batched call equal to the single-row call."""
+    import bit_affine_quantized_qmv_amd as q
+    k, n = 2560, 1
+    qw = _quantized(q, dev, n, k, 64, 8, "bf16", seed=65, std=0.02)
+    x = synth.normal_x((rows, 1, k), "bf16", seed=66).to(dev)
+    y = q.qmv(x, qw)
+    assert y.shape == (rows, 1, 1)
+    assert_close(y.reshape(rows, 1), reference_rows(values(x).reshape(rows, k), qw, "bf16"), "K=2560 N=1")
+    for r in range(rows):
+        assert torch.equal(q.qmv(x[r], qw)[0], y[r, 0]), r
+
+
+# Shapes that reach each decode kernel path: whole rows at short K, rows cut into parts
+# (long K at 4 and 8 bits), activations too large for LDS (K processed in chunks), and
+# 17-32 rows at long K (two 16-row passes).
+DET_CASES = [
+    # (bits, gs, k, n, rows)
+    (4, 64, 1024, 2000, 32),
+    (4, 64, 2048, 1000, 8),
+    (4, 64, 3072, 1000, 32),
+    (8, 64, 1024, 1000, 16),
+    (8, 32, 1408, 700, 32),
+    (4, 32, 4096, 600, 32),
+    (4, 128, 8192, 500, 16),
+    (2, 32, 640, 1000, 16),
+    (6, 32, 640, 1000, 1),
+    (5, 64, 4096, 500, 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DET_CASES)))
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_repeated_calls_bitwise_equal_all_paths(dev, case, dtype):
+    """Identical calls give identical bits on every decode path (a kernel that reads
+    uninitialized LDS, registers or output memory, or races between waves, fails this)."""
+    import bit_affine_quantized_qmv_amd as q
+    bits, gs, k, n, rows = DET_CASES[case]
+    qw = _quantized(q, dev, n, k, gs, bits, dtype, seed=70 + case)
+    x = synth.normal_x((rows, k), dtype, seed=71 + case).to(dev)
+    ref = q.qmv(x, qw).clone()
+    assert_close(ref, reference_rows(values(x), qw, dtype), DET_CASES[case])
+    for _ in range(8):
+        junk = torch.full_like(ref, float("nan"))
+        del junk
+        y = q.qmv(x, qw)
+        assert torch.equal(y, ref), (DET_CASES[case], dtype)
