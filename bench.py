@@ -4,9 +4,14 @@
 Headline: lm_head decode qmv (x [32,1,1024] bf16, W [151936,1024] 4-bit, group 64), as
 effective HBM GB/s = algorithmic bytes (packed W + scales + biases + x + y) per call /
 time.  The same JSON line carries the prefill qmm_t figure (x [4,512,4096] bf16,
-W [14336,4096] 4-bit, group 128) in TFLOP/s, the per-kernel roofline (kernel duration
-from HIP events on the launch stream) and the CPU oracle timed on a bounded sample.
+W [14336,4096] 4-bit, group 128) in TFLOP/s, the per-kernel roofline, the small decode
+configurations with the launch floor, a paired comparison of the per-batch-element
+launch against the folded one, and the CPU oracle timed on a bounded sample.
 
+Timing: the K timed steps are captured once into a HIP graph; one replay of that graph is
+the timed region.  `ms_per_step` is its host wall time (synchronize on both sides) / K;
+the roofline's `kernel_ms` is the device time between two events recorded on the launch
+stream around the same replay / K, i.e. the average duration of back-to-back launches.
 Inputs are resident in HBM before timing starts; each step uses the next of several
 weight/activation copies whose total exceeds the 256 MB Infinity Cache, so weights come
 from HBM every call.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -75,86 +80,99 @@ def _profile_field(summary_name, tag, kernel_sources, field):
 
 
 def _time_steps(fn, steps, warmup, torch, use_graph=True):
-    """Times `steps` calls of fn(i) three ways:
+    """Times `steps` calls fn(0), ..., fn(steps - 1).
 
-    wall_ms    -- the steps captured once into a HIP graph, whose replay is bracketed by
-                  torch.cuda.synchronize() on both sides (host wall clock per step);
-    kernel_ms  -- the same steps launched eagerly behind untimed launches of the same step,
-                  so the queue stays ahead of the host, with an event pair around every
-                  launch on the launch stream (mean / median / p10 / p90 of the per-launch
-                  durations);
-    eager_ms   -- the steps launched eagerly from Python with synchronize on both sides
-                  (includes the host's per-call marshalling; context only).
+    The calls are captured once into a HIP graph; after one untimed replay, one replay is
+    timed two ways: wall_ms = host wall clock with torch.cuda.synchronize() on both sides,
+    kernel_ms = elapsed time of two events recorded on the launch stream around it (the
+    average device duration of the back-to-back launches, launch gaps included), both per
+    step.  eager_ms: the same calls launched from Python (host marshalling included;
+    context only).  Without a graph, both figures come from eager launches.
     """
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-
     t0 = time.perf_counter()
     for i in range(steps):
         fn(i)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     graph_ok = use_graph
-    try:
-        if not use_graph:
-            raise RuntimeError("graph timing disabled")
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn(0)                      # launch-side caches are filled outside capture
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                fn(i)
-        g.replay()
+    if use_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn(0)                      # launch-side caches are filled outside capture
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+            del g
+        except Exception:          # timing only: fall back to eager launches
+            graph_ok = False
+    if not graph_ok:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        g.replay()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        del g
-    except Exception:              # timing only: report the eager figure instead
-        graph_ok = False
-        wall_ms = eager_ms
-
-    # The queue is primed with untimed launches of the same step, enough GPU work to cover
-    # the host's enqueue time of the timed launches, so those run back to back at the
-    # clock the device holds under this load.  (A spin kernel as the primer lets the clock
-    # drop: the prefill kernel then averaged ~270 us instead of ~225 us.)
-    torch.cuda.synchronize()
-    host_ms = 3.0 * eager_ms * steps + 5.0
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(int(host_ms / max(min(wall_ms, eager_ms), 1e-3)) + 1):
-        fn(i)
-    for i in range(steps):
-        starts[i].record()
-        fn(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    kern = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    span_ms = starts[0].elapsed_time(ends[-1]) / steps
-    q = lambda f: kern[min(len(kern) - 1, int(f * len(kern)))]
-    return {"wall_ms": wall_ms, "graph": graph_ok, "eager_ms": eager_ms,
-            "queued_span_ms": span_ms, "kernel_mean_ms": sum(kern) / len(kern),
-            "kernel_median_ms": q(0.5), "kernel_p10_ms": q(0.1), "kernel_p90_ms": q(0.9)}
+    kernel_ms = start.elapsed_time(end) / steps
+    return {"wall_ms": wall_ms, "kernel_ms": kernel_ms, "graph": graph_ok, "eager_ms": eager_ms}
 
 
-def _cpu_threads():
+def _host_info():
+    """The host the oracle is timed on: CPU model, usable cores, numpy and its BLAS."""
+    import numpy as np
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = "%s %s" % (b.get("name", ""), b.get("version", ""))
+    except Exception:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": cores, "numpy": np.__version__, "blas": blas.strip()}
+
+
+def _blas_threads():
+    """Threads of the BLAS pool numpy's products run on (loaded pools only)."""
     try:
         from threadpoolctl import threadpool_info
-        n = max((p.get("num_threads") or 1) for p in threadpool_info()) if threadpool_info() else 1
-        return int(n)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(int(p.get("num_threads") or 1) for p in pools) if pools else 1
     except Exception:
-        return os.cpu_count() or 1
+        return 1
 
 
 def _oracle_rate(run_sample, budget_s):
-    """Time the oracle on growing samples until ~budget_s of CPU work; returns (units/s, desc)."""
+    """Time the oracle on successive samples until ~budget_s of CPU work; returns
+    (units/s, sample description, samples run)."""
     done_units, spent, desc = 0.0, 0.0, ""
     i = 0
     while spent < budget_s:
@@ -169,16 +187,15 @@ def _oracle_rate(run_sample, budget_s):
 
 def _leg(metric, amount, t, bound, unit, peak, kernel, config):
     """One measured leg: `amount` algorithmic bytes (GB/s legs) or flops (TFLOP/s legs) per call,
-    over the graph-replay step time (value) and the event-timed launch duration (roofline)."""
+    over the graph-replay step time (value) and the device time of the same replay (roofline)."""
     scale = 1e9 if unit == "GB/s" else 1e12
     value = amount / (t["wall_ms"] * 1e-3) / scale
-    achieved = amount / (t["kernel_mean_ms"] * 1e-3) / scale
+    achieved = amount / (t["kernel_ms"] * 1e-3) / scale
     return {"metric": metric, "value": round(value, 1), "unit": unit, "ms_per_step": round(t["wall_ms"], 5),
             "config": config,
             "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                          "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel,
-                         "kernel_ms_mean": round(t["kernel_mean_ms"], 5),
-                         "kernel_ms_median": round(t["kernel_median_ms"], 5)}}
+                         "kernel_ms": round(t["kernel_ms"], 5)}}
 
 
 def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
@@ -256,17 +273,99 @@ def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
     del uq, ux, uy, dx, dy
 
 
+def _small_legs(args, q, torch, dev, synth, floor_ms):
+    """The small decode configurations (probe, batched decode projections, odd N) and the
+    lm_head weight at one activation row.  The small ones move 0.5-3.6 MB per call, less
+    than a microsecond of HBM time, so they are reported with the launch floor beside them;
+    64 weight copies are rotated so the weights do not stay in the L2."""
+    out = {"launch_floor_us": round(floor_ms * 1e3, 2), "legs": []}
+    steps = max(20, args.steps // 4)
+
+    def leg(name, x, qw0, entry, nbytes, copies=64, flops=None):
+        qws = [qw0] + [q.QuantizedWeight(qw0.w_packed.clone(), qw0.scales.clone(), qw0.biases.clone(), qw0.N, qw0.K,
+                                         qw0.group_size, qw0.bits) for _ in range(copies - 1)]
+        ys = [torch.empty(*x.shape[:-1], qw0.N, dtype=x.dtype, device=dev) for _ in range(4)]
+        fn = (lambda i: q.qmv(x, qws[i % copies], out=ys[i % 4])) if entry == "qmv" else \
+             (lambda i: q.qmm_t(x, qws[i % copies], out=ys[i % 4]))
+        t = _time_steps(fn, steps, 3, torch, not args.no_graph)
+        r = {"workload": name, "us_per_call": round(t["wall_ms"] * 1e3, 2),
+             "kernel_us": round(t["kernel_ms"] * 1e3, 2), "algorithmic_bytes": nbytes,
+             "GB/s": round(nbytes / (t["kernel_ms"] * 1e-3) / 1e9, 1),
+             "frac_hbm_peak": round(nbytes / (t["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        out["legs"].append(r)
+        del qws, ys
+
+    def nbytes_of(n, k, bits, gs, m):
+        return n * k * bits // 8 + 2 * n * (k // gs) * 2 + m * k * 2 + m * n * 2
+
+    # the issue-47331 probe: W [1024, 2048] 4-bit group 64 bf16, x [2,K], [2,1,K], [2,4,K]
+    qp = q.quantize(synth.probe_weight().to(dev), 64, 4, "bf16")
+    for shape in ((2, 2048), (2, 1, 2048), (2, 4, 2048)):
+        x = synth.normal_x(shape, "bf16", seed=1).to(dev)
+        m = x.numel() // 2048
+        leg("probe qmm_t x %s, W [1024,2048] 4-bit g64 bf16" % list(shape), x, qp, "qmm_t",
+            nbytes_of(1024, 2048, 4, 64, m))
+    del qp
+    # batched decode projections, B = 1 and 32, 4- and 8-bit, group 64, bf16
+    for i, (k, n) in enumerate(synth.DECODE_SHAPES):
+        w = synth.normal_weight(n, k, 0.02, seed=100 + i).to(dev)
+        for bits in (4, 8):
+            qw = q.quantize(w, 64, bits, "bf16")
+            for b in (1, 32):
+                x = synth.normal_x((b, 1, k), "bf16", seed=200 + i).to(dev)
+                leg("decode x [%d,1,%d], W [%d,%d] %d-bit g64 bf16" % (b, k, n, k, bits), x, qw, "qmv",
+                    nbytes_of(n, k, bits, 64, b))
+            del qw
+        del w
+    # odd N at K = 4096, x alternating 2048, 1
+    for n in (1, 1001):
+        for bits, gs, dt in ((6, 32, "fp16"), (3, 128, "bf16")):
+            qw = q.quantize(synth.normal_weight(n, 4096, 0.02, seed=400 + n + bits).to(dev), gs, bits, dt)
+            x = synth.alternating_x(4096, dt).to(dev)
+            leg("odd N x [1,4096] alternating, W [%d,4096] %d-bit g%d %s" % (n, bits, gs, dt), x, qw, "qmv",
+                nbytes_of(n, 4096, bits, gs, 1))
+            del qw
+    return out
+
+
+def _paired_ratio(args, q, torch, fold, forced, rounds=8, steps=10):
+    """Paired, A/A-calibrated comparison of the per-batch-element launch against the folded
+    one: each round times the folded call (A), the forced call (B) and the folded call again
+    (A'), each as one graph replay of `steps` calls; the geometric means of B/A and A'/A over
+    the rounds are reported (MLX pull request 4516, "Performance": geometric mean of paired
+    Baseline/Candidate ratios from A/A-calibrated runs)."""
+    import math
+    ab, aa, ta, tb = [], [], [], []
+    for r in range(rounds):
+        t_a = _time_steps(fold, steps, 2, torch, not args.no_graph)["kernel_ms"]
+        t_b = _time_steps(forced, steps, 2, torch, not args.no_graph)["kernel_ms"]
+        t_a2 = _time_steps(fold, steps, 2, torch, not args.no_graph)["kernel_ms"]
+        ab.append(t_b / t_a)
+        aa.append(t_a2 / t_a)
+        ta.append(t_a)
+        tb.append(t_b)
+    gm = lambda v: math.exp(sum(math.log(x) for x in v) / len(v))
+    return {"rounds": rounds, "steps_per_timing": steps,
+            "forced_over_folded_geomean": round(gm(ab), 3),
+            "forced_over_folded_range": [round(min(ab), 3), round(max(ab), 3)],
+            "aa_geomean": round(gm(aa), 4), "aa_range": [round(min(aa), 4), round(max(aa), 4)],
+            "folded_kernel_ms_median": round(sorted(ta)[len(ta) // 2], 5),
+            "forced_kernel_ms_median": round(sorted(tb)[len(tb) // 2], 5),
+            "pages_apple_m4max_ms": {"batched_grid_z": 60.0, "flattened": 2.2}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing per leg")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle timing per phase")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["qmv", "qmm_t", "next", "all"], default="all",
+    ap.add_argument("--only", choices=["qmv", "qmm_t", "next", "small", "forced", "all"], default="all",
                     help="legs besides the headline qmv: the prefill qmm_t, the next rows "
-                         "(gathered qmv, fused argmax, dequantize, embedding, unaligned K), or all")
+                         "(gathered qmv, fused argmax, dequantize, embedding, unaligned K), the small "
+                         "configurations, the per-batch-element launch alone (for counters), or all")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps eagerly instead of replaying them from a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -309,13 +408,17 @@ def main():
     xs = [x0.clone() for _ in range(copies)]
     ys = [torch.empty(m, 1, n, dtype=x0.dtype, device=dev) for _ in range(copies)]
     qmv_bytes = n * k * bits // 8 + 2 * n * (k // gs) * 2 + m * k * 2 + m * n * 2
+    if args.only == "forced":
+        # the per-batch-element launch alone (32 grid slices of one row each), for counters
+        t = _time_steps(lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED,
+                                        out=ys[i % copies]), args.steps, args.warmup, torch, not args.no_graph)
+        print(json.dumps({"metric": "forced per-batch-element lm_head decode", "kernel_ms": t["kernel_ms"],
+                          "ms_per_step": t["wall_ms"], "steps": args.steps}))
+        return
     t = _time_steps(lambda i: q.qmv(xs[i % copies], qws[i % copies], out=ys[i % copies]),
                     args.steps, args.warmup, torch, not args.no_graph)
-    tf = _time_steps(lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED,
-                                     out=ys[i % copies]), max(10, args.steps // 4), 3, torch,
-                    not args.no_graph)
     qmv_value = qmv_bytes / (t["wall_ms"] * 1e-3) / 1e9
-    achieved = qmv_bytes / (t["kernel_mean_ms"] * 1e-3) / 1e9
+    achieved = qmv_bytes / (t["kernel_ms"] * 1e-3) / 1e9
     line = {
         "metric": "qmv effective HBM GB/s (lm_head decode)",
         "value": round(qmv_value, 1),
@@ -332,24 +435,37 @@ def main():
         "config": {"workload": "lm_head decode qmv: x [32,1,1024] bf16, W [151936,1024] 4-bit "
                                "group 64 bf16 scales/biases, folded to one 2D call",
                    "algorithmic_bytes_per_call": qmv_bytes, "weight_copies_rotated": copies,
-                   "timing": "K steps captured in one HIP graph, replay bracketed by synchronize"
+                   "timing": "K steps captured in one HIP graph, one replay bracketed by synchronize"
                              if t["graph"] else "K eager steps bracketed by synchronize",
                    "pct_hbm_peak": round(100 * qmv_value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("qmv_stream_kernel_lm_head_traffic.md", QMV_SOURCES),
                      "kernel": "qmv_stream_kernel",
-                     "kernel_ms_mean": round(t["kernel_mean_ms"], 5),
-                     "kernel_ms_median": round(t["kernel_median_ms"], 5),
-                     "kernel_ms_p10_p90": [round(t["kernel_p10_ms"], 5), round(t["kernel_p90_ms"], 5)]},
-        "context": {"eager_python_ms_per_step": round(t["eager_ms"], 5),
-                    "forced_strided_32x1_kernel_ms": round(tf["kernel_mean_ms"], 5),
-                    "forced_vs_folded": round(tf["kernel_mean_ms"] / t["kernel_mean_ms"], 2),
-                    "pages_apple_m4max_ms": {"batched_grid_z": 60.0, "flattened": 2.2}},
+                     "kernel_ms": round(t["kernel_ms"], 5),
+                     "kernel_ms_source": "events on the launch stream around the timed graph replay, per step"},
+        "context": {"eager_python_ms_per_step": round(t["eager_ms"], 5)},
     }
     out["qmv"] = line
     nsteps = max(10, args.steps // 4)
     nwarm = max(3, args.warmup // 4)
+    if args.only in ("all", "qmv"):
+        # the per-batch-element launch (32 grid slices, each re-reading W) against the folded call
+        line["context"]["forced_vs_folded"] = _paired_ratio(
+            args, q, torch, lambda i: q.qmv(xs[i % copies], qws[i % copies], out=ys[i % copies]),
+            lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED, out=ys[i % copies]))
+        # the same weight at one activation row
+        x1 = [synth.normal_x((1, k), cfg["dtype"], seed=cfg["x_seed"]).to(dev) for _ in range(copies)]
+        y1 = [torch.empty(1, n, dtype=x0.dtype, device=dev) for _ in range(copies)]
+        b1 = n * k * bits // 8 + 2 * n * (k // gs) * 2 + k * 2 + n * 2
+        t1 = _time_steps(lambda i: q.qmv(x1[i % copies], qws[i % copies], out=y1[i % copies]), args.steps,
+                         args.warmup, torch, not args.no_graph)
+        line["context"]["lm_head_one_row"] = _leg(
+            "qmv effective HBM GB/s (lm_head decode, one row)", b1, t1, "hbm", "GB/s", HBM_PEAK_GBS,
+            "qmv_stream_kernel",
+            {"workload": "lm_head decode qmv: x [1,1024] bf16, W [151936,1024] 4-bit group 64 bf16",
+             "algorithmic_bytes_per_call": b1})
+        del x1, y1
     if args.only in ("all", "next"):
         out["next"] = {}
         # fused argmax on the lm_head logits, with and without storing them
@@ -391,7 +507,7 @@ def main():
         obytes = m * n * 2 + m * tk * 8
         topk_rows["topk_alone"] = _leg(
             "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_parts_kernel",
-            {"workload": "per-row top-50 of [32,151936] bf16 logits (19 column chunks per row)",
+            {"workload": "per-row top-50 of [32,151936] bf16 logits (column chunks per row)",
              "algorithmic_bytes_per_call": obytes})
         out["next"]["topk"] = topk_rows
         # quantized embedding gather from the lm_head table
@@ -408,7 +524,17 @@ def main():
             {"workload": "embedding: 2048 seeded token rows of the [151936,1024] 4-bit group 64 bf16 table "
                          "-> [2048,1024] bf16", "algorithmic_bytes_per_call": ebytes})
         del idxs, eouts
-    del qws, xs, ys, w
+    del qws, xs, ys
+
+    if args.only in ("all", "small"):
+        # launch floor: graph replay of a one-tile decode call (N = 16, K = 128)
+        qf = q.quantize(synth.normal_weight(16, 128, 1.0, seed=5).to(dev), 64, 4, "bf16")
+        xf = synth.normal_x((1, 128), "bf16", seed=5).to(dev)
+        yf = torch.empty(1, 16, dtype=torch.bfloat16, device=dev)
+        tfl = _time_steps(lambda i: q.qmv(xf, qf, out=yf), args.steps, 5, torch, not args.no_graph)
+        out["small"] = _small_legs(args, q, torch, dev, synth, tfl["kernel_ms"])
+        out["small"]["launch_floor_workload"] = "one 16x128 4-bit tile, x [1,128]: device time per launch"
+        del qf, xf, yf
 
     # ------------------------------------------------------------ prefill qmm_t
     if args.only in ("all", "qmm_t"):
@@ -432,19 +558,19 @@ def main():
         pv = _time_steps(lambda i: q.qmm_t(view, pqs[i % pcopies], out=pys[i % pcopies]),
                          max(5, psteps // 2), 2, torch, not args.no_graph)
         tflops = flops / (pt["wall_ms"] * 1e-3) / 1e12
-        ach = flops / (pt["kernel_mean_ms"] * 1e-3) / 1e12
+        ach = flops / (pt["kernel_ms"] * 1e-3) / 1e12
         out["qmm_t"] = {
             "metric": "qmm_t TFLOP/s (prefill)", "value": round(tflops, 1), "unit": "TFLOP/s",
             "steps": psteps, "ms_per_step": round(pt["wall_ms"], 5), "dtype": "bf16",
             "config": {"workload": "prefill qmm_t: x [4,512,4096] bf16, W [14336,4096] 4-bit group 128 "
                                    "bf16 scales/biases, y [4,512,14336]",
                        "flops_per_call": flops, "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
-                       "narrowed_view_kernel_ms": round(pv["kernel_mean_ms"], 5)},
+                       "narrowed_view_kernel_ms": round(pv["kernel_ms"], 5)},
             "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": _traffic("qmm_prefill_dma_kernel_prefill_traffic.md", QMM_T_SOURCES),
-                         "kernel": "qmm_prefill_dma_kernel", "kernel_ms_mean": round(pt["kernel_mean_ms"], 5),
-                         "kernel_ms_median": round(pt["kernel_median_ms"], 5),
+                         "kernel": "qmm_prefill_dma_kernel", "kernel_ms": round(pt["kernel_ms"], 5),
+                         "kernel_ms_source": "events on the launch stream around the timed graph replay, per step",
                          # matrix-core busy fraction from the SQ_VALU_MFMA_BUSY_CYCLES counter
                          "mfma_util_counter": _profile_field("qmm_prefill_dma_kernel_prefill_mfma_util.md",
                                                              "mfma-util-json", QMM_T_SOURCES, "mfma_util")},
@@ -456,64 +582,105 @@ def main():
 
     # ------------------------------------------------------------ CPU oracle baselines
     if not args.no_cpu_baseline:
-        import oracle as O
-        threads = _cpu_threads()
-        qw_h = {"w": qw0.w_packed.cpu().numpy().view(np.uint32),
-                "s": qw0.scales.cpu().view(torch.int16).numpy().view(np.uint16),
-                "b": qw0.biases.cpu().view(torch.int16).numpy().view(np.uint16)}
-        x_h = x0.float().cpu().numpy().astype(np.float64).reshape(m, k)
-        chunk = 4096
-
-        def qmv_sample(i):
-            lo = (i * chunk) % n
-            hi = min(n, lo + chunk)
-            t0 = time.perf_counter()
-            codes = O.unpack(qw_h["w"][lo:hi], bits, k)
-            wd = O.dequant(codes, qw_h["s"][lo:hi], qw_h["b"][lo:hi], gs, "bf16")
-            O.matmul_rows(x_h, wd)
-            dt = time.perf_counter() - t0
-            rows = hi - lo
-            nbytes = rows * k * bits // 8 + 2 * rows * (k // gs) * 2 + m * k * 2 + m * rows * 2
-            return nbytes / 1e9, dt, "%d-row slices of W with all 32 activation rows" % chunk
-
-        rate, desc, nsamp = _oracle_rate(qmv_sample, args.cpu_budget)
-        out["qmv"]["cpu_baseline"] = {"value": round(rate, 3), "unit": "GB/s", "cores": threads,
-                                      "kind": "oracle",
-                                      "sample": "%s (%d slices: unpack, dequantize, float64 product)"
-                                                % (desc, nsamp)}
+        out["qmv"]["cpu_baseline"] = _cpu_baseline_qmv(args, np, torch, qw0, w, x0, cfg)
         if "qmm_t" in out:
-            pc = synth.PREFILL
-            pq_h = {"w": pq0.w_packed.cpu().numpy().view(np.uint32),
-                    "s": pq0.scales.cpu().view(torch.int16).numpy().view(np.uint16),
-                    "b": pq0.biases.cpu().view(torch.int16).numpy().view(np.uint16)}
-            px_h = px0.float().cpu().numpy().astype(np.float64).reshape(-1, pc["k"])
-            wrows = 2048
-            state = {}
-
-            def qmm_sample(i):
-                t0 = time.perf_counter()
-                if "wd" not in state:
-                    codes = O.unpack(pq_h["w"][:wrows], pc["bits"], pc["k"])
-                    state["wd"] = O.dequant(codes, pq_h["s"][:wrows], pq_h["b"][:wrows],
-                                            pc["group_size"], "bf16")
-                r0 = (i * 64) % px_h.shape[0]
-                O.matmul_rows(px_h[r0:r0 + 64], state["wd"])
-                dt = time.perf_counter() - t0
-                return 2.0 * 64 * wrows * pc["k"] / 1e12, dt, \
-                    "64-row activation blocks against the first %d weight rows" % wrows
-
-            prate, pdesc, pn_s = _oracle_rate(qmm_sample, args.cpu_budget)
-            out["qmm_t"]["cpu_baseline"] = {"value": round(prate, 5), "unit": "TFLOP/s",
-                                            "cores": threads, "kind": "oracle",
-                                            "sample": "%s (%d blocks; unpack+dequantize once, "
-                                                      "float64 product)" % (pdesc, pn_s)}
+            out["qmm_t"]["cpu_baseline"] = _cpu_baseline_qmm_t(args, np, torch, pq0, px0)
 
     line = out["qmv"]
     if "qmm_t" in out:
         line["qmm_t"] = out["qmm_t"]
+    if "small" in out:
+        line["small_configs"] = out["small"]
     if "next" in out:
         line["next_rows"] = out["next"]
     print(json.dumps(line))
+
+
+def _cpu_baseline_qmv(args, np, torch, qw0, w, x0, cfg):
+    """The oracle on the lm_head workload, on bounded samples of weight rows: the per-call
+    path (unpack, dequantize, float64 product against all 32 rows) with every BLAS thread
+    and with one, plus the one-time phases (quantize, unpack + dequantize) on their own."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    n, k, m, bits, gs = cfg["n"], cfg["k"], cfg["m"], cfg["bits"], cfg["group_size"]
+    qw_h = {"w": qw0.w_packed.cpu().numpy().view(np.uint32),
+            "s": qw0.scales.cpu().view(torch.int16).numpy().view(np.uint16),
+            "b": qw0.biases.cpu().view(torch.int16).numpy().view(np.uint16)}
+    x_h = x0.float().cpu().numpy().astype(np.float64).reshape(m, k)
+    w_h = w.numpy()
+    chunk = 4096
+
+    def call_sample(i):
+        lo = (i * chunk) % n
+        hi = min(n, lo + chunk)
+        t0 = time.perf_counter()
+        codes = O.unpack(qw_h["w"][lo:hi], bits, k)
+        wd = O.dequant(codes, qw_h["s"][lo:hi], qw_h["b"][lo:hi], gs, "bf16")
+        O.matmul_rows(x_h, wd)
+        dt = time.perf_counter() - t0
+        rows = hi - lo
+        nbytes = rows * k * bits // 8 + 2 * rows * (k // gs) * 2 + m * k * 2 + m * rows * 2
+        return nbytes / 1e9, dt, "%d-row slices of W with all 32 activation rows" % chunk
+
+    def phase_rate(fn, budget):
+        spent, rows, i = 0.0, 0, 0
+        while spent < budget:
+            lo = (i * chunk) % n
+            hi = min(n, lo + chunk)
+            t0 = time.perf_counter()
+            fn(lo, hi)
+            spent += time.perf_counter() - t0
+            rows += hi - lo
+            i += 1
+        return rows / spent
+
+    rate, desc, nsamp = _oracle_rate(call_sample, args.cpu_budget)
+    threads = _blas_threads()
+    with threadpool_limits(limits=1):
+        rate1, _, nsamp1 = _oracle_rate(call_sample, args.cpu_budget / 2)
+    q_rows = phase_rate(lambda lo, hi: O.quantize(w_h[lo:hi], gs, bits, "bf16"), args.cpu_budget / 4)
+    d_rows = phase_rate(lambda lo, hi: O.dequant(O.unpack(qw_h["w"][lo:hi], bits, k), qw_h["s"][lo:hi],
+                                                 qw_h["b"][lo:hi], gs, "bf16"), args.cpu_budget / 4)
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%s (%d slices: unpack, dequantize, float64 product, %d BLAS threads)"
+                      % (desc, nsamp, threads),
+            "one_thread": {"value": round(rate1, 4), "unit": "GB/s", "cores": 1, "samples": nsamp1},
+            "phases_seconds_for_whole_weight": {"quantize": round(n / q_rows, 2),
+                                                "unpack_dequantize": round(n / d_rows, 2)},
+            "host": _host_info()}
+
+
+def _cpu_baseline_qmm_t(args, np, torch, pq0, px0):
+    """The oracle's product for the prefill workload: 64-row activation blocks against the
+    first 2048 weight rows (unpack and dequantize once), every BLAS thread and one."""
+    import oracle as O
+    import synth
+    from threadpoolctl import threadpool_limits
+    pc = synth.PREFILL
+    pq_h = {"w": pq0.w_packed.cpu().numpy().view(np.uint32),
+            "s": pq0.scales.cpu().view(torch.int16).numpy().view(np.uint16),
+            "b": pq0.biases.cpu().view(torch.int16).numpy().view(np.uint16)}
+    px_h = px0.float().cpu().numpy().astype(np.float64).reshape(-1, pc["k"])
+    wrows = 2048
+    codes = O.unpack(pq_h["w"][:wrows], pc["bits"], pc["k"])
+    wd = O.dequant(codes, pq_h["s"][:wrows], pq_h["b"][:wrows], pc["group_size"], "bf16")
+
+    def block_sample(i):
+        t0 = time.perf_counter()
+        r0 = (i * 64) % px_h.shape[0]
+        O.matmul_rows(px_h[r0:r0 + 64], wd)
+        dt = time.perf_counter() - t0
+        return 2.0 * 64 * wrows * pc["k"] / 1e12, dt, "64-row activation blocks against the first %d weight rows" % wrows
+
+    prate, pdesc, pn_s = _oracle_rate(block_sample, args.cpu_budget)
+    threads = _blas_threads()
+    with threadpool_limits(limits=1):
+        prate1, _, pn1 = _oracle_rate(block_sample, args.cpu_budget / 2)
+    return {"value": round(prate, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%s (%d blocks; unpack + dequantize once, float64 product, %d BLAS threads)"
+                      % (pdesc, pn_s, threads),
+            "one_thread": {"value": round(prate1, 5), "unit": "TFLOP/s", "cores": 1, "samples": pn1},
+            "host": _host_info()}
 
 
 if __name__ == "__main__":

@@ -51,13 +51,19 @@ def test_committed_summaries_carry_a_hash_and_positive_figures():
 
 
 def test_leg_divides_algorithmic_amount_by_the_two_times():
-    t = {"wall_ms": 0.5, "kernel_mean_ms": 0.4, "kernel_median_ms": 0.39}
+    t = {"wall_ms": 0.5, "kernel_ms": 0.4}
     leg = bench._leg("m", 2.0e9, t, "hbm", "GB/s", 8000.0, "k", {"workload": "w"})
     assert leg["value"] == pytest.approx(4000.0)            # 2 GB over 0.5 ms
     roof = leg["roofline"]
     assert roof["achieved"] == pytest.approx(5000.0)        # 2 GB over 0.4 ms
     assert roof["frac"] == pytest.approx(5000.0 / 8000.0)
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert roof["kernel_ms"] == pytest.approx(0.4)
     flops = bench._leg("m", 2.5e12, t, "mfma", "TFLOP/s", 2500.0, "k", {"workload": "w"})
     assert flops["value"] == pytest.approx(5000.0)          # 2.5 TFLOP over 0.5 ms
     assert flops["roofline"]["frac"] == pytest.approx(6250.0 / 2500.0)
+
+
+def test_host_info_names_the_cpu_and_blas():
+    info = bench._host_info()
+    assert info["nproc"] >= 1 and isinstance(info["cpu_model"], str) and info["numpy"]
