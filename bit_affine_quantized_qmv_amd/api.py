@@ -176,6 +176,39 @@ def qmv_argmax(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, worksp
     return idx, val, y
 
 
+def qmv_argmax_noalloc(x: torch.Tensor, qw: QuantizedWeight, logits: bool = True, out=None, out_index=None,
+                       out_value=None):
+    """qmv_argmax without a workspace (qmm_qmv_argmax_noalloc): the library's own device
+    array serves as the workspace, so the call allocates nothing when the outputs are given.
+    Calls on one GPU that may overlap (different streams) race on that array."""
+    lib = _lib.load()
+    rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
+    if not logits:
+        y = None
+    elif out is not None:
+        y = out
+        assert y.dtype == x.dtype and y.is_contiguous() and tuple(y.shape) == tuple(x.shape[:-1]) + (qw.N,)
+    else:
+        y = torch.empty(*x.shape[:-1], qw.N, dtype=x.dtype, device=x.device)
+    shape = list(x.shape[:-1]) + [qw.N]
+    strides, acc = [], 1
+    for s in reversed(shape):
+        strides.insert(0, acc)
+        acc *= s
+    yd = _lib.tensor_desc(shape, strides)
+    idx = out_index if out_index is not None else torch.empty(rows, dtype=torch.int32, device=x.device)
+    val = out_value if out_value is not None else torch.empty(rows, dtype=torch.float32, device=x.device)
+    assert idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() >= rows
+    assert val.dtype == torch.float32 and val.is_contiguous() and val.numel() >= rows
+    if x.dtype != qw.dtype:
+        raise _lib.QmmError(-2, "x, scales and biases must share one dtype")
+    xd = _lib.tensor_desc(x.shape, x.stride())
+    _lib.check(lib.qmm_qmv_argmax_noalloc(x.data_ptr(), ctypes.byref(xd), ctypes.byref(qw.desc()),
+                                          y.data_ptr() if y is not None else None, ctypes.byref(yd), idx.data_ptr(),
+                                          val.data_ptr(), _stream(x.device)))
+    return idx, val, y
+
+
 def _dtype_code(dtype) -> int:
     if dtype == torch.bfloat16:
         return _lib.QMM_BF16

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmm.so")
-SOURCES = ["decode_b4.hip", "decode_b8.hip", "decode_bn.hip", "decode.cpp", "prefill.hip", "dequant.hip", "quantize.hip", "topk.hip", "dispatch.cpp", "capi.cpp"]
+SOURCES = ["decode_b4.hip", "decode_b8.hip", "decode_bn.hip", "decode.cpp", "prefill.hip", "dequant.hip", "quantize.hip", "topk.hip", "noalloc.hip", "dispatch.cpp", "capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed float32 instructions stay disabled for every device pass.

@@ -5,6 +5,7 @@
 #include <string>
 
 #include "../../include/qmm.h"
+#include "capi_internal.hpp"
 #include "dispatch.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -68,6 +69,38 @@ int32_t check_topk(int32_t dtype, int64_t n, int64_t row_stride, int32_t k) {
 }
 
 }  // namespace
+
+namespace qmm {
+
+int32_t report(int32_t rc, const std::string& msg) { return finish(rc, msg); }
+
+int32_t report_launch(hipError_t e) { return launch_status(e); }
+
+int32_t prepare_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                           const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, MatArgs* out,
+                           int64_t* rows) {
+  std::string err;
+  qmm_plan_t p;
+  *rows = 0;
+  // y may be NULL (no logits stored); validate the call with a stand-in output pointer
+  static char y_stand_in alignas(16);
+  int rc = plan_matmul(x, x_desc, w, y ? y : (void*)&y_stand_in, y_desc, 0, 0, true, &p, &err);
+  if (rc != QMM_OK) return finish(rc, err);
+  if (p.rows == 0) return finish(QMM_OK, "");
+  if (w->w_row_stride % 4)
+    return finish(QMM_ERR_ALIGN, "qmv_argmax: needs w_row_stride a multiple of 4 words");
+  if (!out_index) return finish(QMM_ERR_NULL, "qmv_argmax: out_index must be non-NULL");
+  if ((uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
+    return finish(QMM_ERR_ALIGN, "qmv_argmax: out_index/out_value must be 4-byte aligned");
+  if (w->N == 0 || w->N >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "qmv_argmax: need 0 < N < 2^31");
+  *out = make_args(x, p, w, y);
+  out->argmax_index = out_index;
+  out->argmax_value = out_value;
+  *rows = p.rows;
+  return finish(QMM_OK, "");
+}
+
+}  // namespace qmm
 
 extern "C" {
 
@@ -140,24 +173,14 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
 int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                        const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
                        void* stream) {
-  std::string err;
-  qmm_plan_t p;
-  // y may be NULL (no logits stored); validate the call with a stand-in output pointer
-  static char y_stand_in alignas(16);
-  int rc = qmm::plan_matmul(x, x_desc, w, y ? y : (void*)&y_stand_in, y_desc, 0, 0, true, &p, &err);
-  if (rc != QMM_OK) return finish(rc, err);
-  if (p.rows == 0) return finish(QMM_OK, "");
-  if (w->w_row_stride % 4)
-    return finish(QMM_ERR_ALIGN, "qmv_argmax: needs w_row_stride a multiple of 4 words");
-  if (!out_index || !workspace) return finish(QMM_ERR_NULL, "qmv_argmax: out_index and workspace must be non-NULL");
-  if ((uintptr_t)workspace % 8 || (uintptr_t)out_index % 4 || (uintptr_t)out_value % 4)
-    return finish(QMM_ERR_ALIGN, "qmv_argmax: workspace must be 8-byte, out_index/out_value 4-byte aligned");
-  if (w->N == 0 || w->N >= (1ll << 31)) return finish(QMM_ERR_SHAPE, "qmv_argmax: need 0 < N < 2^31");
-  qmm::MatArgs a = make_args(x, p, w, y);
+  qmm::MatArgs a;
+  int64_t rows = 0;
+  const int32_t rc = qmm::prepare_qmv_argmax(x, x_desc, w, y, y_desc, out_index, out_value, &a, &rows);
+  if (rc != QMM_OK || rows == 0) return rc;
+  if (!workspace) return finish(QMM_ERR_NULL, "qmv_argmax: workspace must be non-NULL");
+  if ((uintptr_t)workspace % 8) return finish(QMM_ERR_ALIGN, "qmv_argmax: workspace must be 8-byte aligned");
   a.argmax_keys = (unsigned long long*)workspace;
-  a.argmax_count = (unsigned int*)(a.argmax_keys + p.rows);
-  a.argmax_index = out_index;
-  a.argmax_value = out_value;
+  a.argmax_count = (unsigned int*)(a.argmax_keys + rows);
   return launch_status(qmm::launch_decode(a, (hipStream_t)stream));
 }
 

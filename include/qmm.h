@@ -11,7 +11,9 @@
  *   - All data pointers are DEVICE pointers.  Descriptors are HOST pointers, read during the
  *     call only.  The caller owns all memory; the library allocates no device memory.  Its
  *     host state is a thread-local error message and, per device, cached launch settings
- *     (kernel LDS limits, occupancies), guarded so that calls from several threads are safe.
+ *     (kernel LDS limits, occupancies) and the address of its one static device array (the
+ *     workspace of qmm_qmv_argmax_noalloc), guarded so that calls from several threads are
+ *     safe.
  *   - Strides are in elements.  A tensor pointer points at the view's first element (a view's
  *     storage offset is already applied).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued asynchronously;
@@ -191,6 +193,21 @@ int32_t qmm_gather_qmv(const void* x, const qmm_tensor_desc_t* x_desc, const qmm
 int32_t qmm_qmv_argmax(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                        const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* workspace,
                        void* stream);
+
+/* The same call as qmm_qmv_argmax without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The workspace is a library-owned device array of
+ * QMM_NOALLOC_MAX_ROWS + 1 eight-byte words per GPU (512 bytes), kept until the process ends;
+ * its device address is looked up once per device, on the first call made there.  Each call
+ * enqueues a small kernel that zeroes the words it uses, then the decode kernel; nothing is
+ * allocated or freed.  Calls on one GPU share that array: calls in stream order are fine,
+ * calls that may run at the same time (different streams) race and give wrong results.
+ * More than QMM_NOALLOC_MAX_ROWS collapsed activation rows -> QMM_ERR_SHAPE (the decode
+ * family takes at most QMM_DECODE_MAX_ROWS anyway).  Results are bitwise those of
+ * qmm_qmv_argmax; contract otherwise as for it. */
+#define QMM_NOALLOC_MAX_ROWS 32
+int32_t qmm_qmv_argmax_noalloc(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
+                               const qmm_tensor_desc_t* y_desc, int32_t* out_index, float* out_value, void* stream);
 
 /* Per-row top-k of stored logits (the top-k form of the decode epilogue on lm_head logits;
  * transformers issue 47331, "Reproduction": the next-token choice that collapses to token
