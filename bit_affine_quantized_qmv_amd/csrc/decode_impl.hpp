@@ -442,12 +442,9 @@ __device__ inline uint32_t pair_lane_half(const SbRegs<KG>& first, const SbRegs<
 // Slots per bias MFMA, the same in every decode kernel so that they agree bit for bit: two
 // when the groups are 64 or 128 codes (two or one per 128-code slot) and the slots per
 // row are even, else one.
-#ifndef QMM_MAX_BLOCK_SLOTS
-#define QMM_MAX_BLOCK_SLOTS 2
-#endif
 template <int GS>
 __device__ inline int bias_span(int slots_per_row) {
-  return (QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
+  return (GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
 }
 
 // Parts per row: the largest power of two <= min(8, slots/8), at least 1 (rows of at most
@@ -462,7 +459,7 @@ __host__ __device__ inline int row_parts(int64_t K) {
 }
 
 // Sub-block size (slots) the decode kernels use for a row of nit slots.
-__host__ __device__ inline int block_slots(int nit) { return (QMM_MAX_BLOCK_SLOTS >= 2 && nit % 2 == 0) ? 2 : 1; }
+__host__ __device__ inline int block_slots(int nit) { return nit % 2 == 0 ? 2 : 1; }
 
 // Slots per part: the slots rounded up to a multiple of P * D, divided by P (a part may
 // reach past the row's last slot; those slots add nothing).
@@ -575,31 +572,31 @@ __device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int mask
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Merge a workgroup's key for one row into the global key.  The atomic returns the old key
-// and the value is consumed, so the thread waits until the merge has been performed at the
-// device-wide point where every workgroup's atomics on the key are ordered.
+// Merge a workgroup's key for one row into the global key (a device-scope atomic maximum;
+// argmax_complete orders it before the workgroup counts itself done).
 __device__ inline void argmax_publish(unsigned long long* key, unsigned long long v) {
-  const unsigned long long old = __hip_atomic_fetch_max(key, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("" ::"v"(old));
+  __hip_atomic_fetch_max(key, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Completion of the fused argmax inside the decode kernel.  Every workgroup, once all its
-// threads have published their row keys (argmax_publish), counts itself done; the last one to
-// count turns each row's key into (index, value) and sets the keys and the counter back to
-// zero, so the workspace is all-zero again when the kernel ends.  Every access to the keys and
-// the counter is a device-scope atomic, so no cache write-back is needed: a key merge is
-// performed before its workgroup counts itself, and the last workgroup reads the keys after
-// its count has returned.  `last` is a workgroup-shared word that is free once every thread
-// has arrived here (it is first written after the barrier below).  Called by every thread.
+// Completion of the fused argmax inside the decode kernel.  Every thread's key merges
+// (argmax_publish) are ordered before its workgroup counts itself done by a release fence at
+// device scope and the workgroup barrier; the count is an acquire-release read-modify-write;
+// the last workgroup to count issues an acquire fence at device scope in every thread before
+// it reads the keys.  That workgroup turns each row's key into (index, value) and sets the
+// keys and the counter back to zero, so the workspace is all-zero again when the kernel
+// ends.  `last` is a workgroup-shared word that is free once every thread has arrived here
+// (it is first written after the barrier below).  Called by every thread.
 __device__ inline void argmax_complete(const MatArgs& a, int64_t total_rows, unsigned* last) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned wgs = gridDim.x * gridDim.y * gridDim.z;
-    const unsigned done = __hip_atomic_fetch_add(a.argmax_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned done = __hip_atomic_fetch_add(a.argmax_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     *last = done + 1 == wgs ? 1u : 0u;
   }
   __syncthreads();
   if (*last == 0u) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int64_t i = threadIdx.x; i < total_rows; i += blockDim.x) {
     const unsigned long long k =
         __hip_atomic_exchange(&a.argmax_keys[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -607,7 +604,7 @@ __device__ inline void argmax_complete(const MatArgs& a, int64_t total_rows, uns
     a.argmax_index[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
     if (a.argmax_value) a.argmax_value[i] = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
   }
-  if (threadIdx.x == 0) __hip_atomic_exchange(a.argmax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(a.argmax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Reduce the wave's keys over the 16 columns of each lane group and merge them into the
@@ -645,33 +642,6 @@ __device__ inline void store_tile(const f32x4 (&acc)[MT], uint16_t* yb, int rows
       const int m = mt * 16 + 4 * lg + r;
       if (m < rows) yb[(int64_t)m * N + n] = T::from_f32(acc[mt][r]);
     }
-}
-
-// Store of a full tile pair through a per-wave LDS area (MROWS rows of kYRow halfwords):
-// the lanes write their fragment values, then each lane stores MROWS bytes of one output
-// row with 16-byte stores.  Needs 16-byte aligned output rows.  The area is private to the
-// wave, whose LDS operations complete in order, so no barrier is involved.
-constexpr int kYRow = 40;   // 32 values of a row + 8 halfwords of padding (80 bytes)
-
-template <class T, int MT, int TN>
-__device__ inline void store_pair_lds(const f32x4 (&acc)[TN][MT], uint16_t* ys, uint16_t* yb, int rows, int64_t n0,
-                                      int64_t N, int lane, int lg, int col) {
-  static_assert(TN == 2, "a pair is 32 output columns");
-  constexpr int MROWS = 16 * MT;
-#pragma unroll
-  for (int t = 0; t < TN; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ys[(mt * 16 + 4 * lg + r) * kYRow + t * 16 + col] = T::from_f32(acc[t][mt][r]);
-  constexpr int kPer = MROWS / 16;          // 16-byte pieces per lane (a row holds 4 pieces)
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int piece = lane * kPer + i;      // row piece / 4, column block piece % 4
-    const int m = piece >> 2, qd = piece & 3;
-    const u32x4 v = *(const u32x4*)(ys + m * kYRow + qd * 8);
-    if (m < rows) *(u32x4*)(yb + (int64_t)m * N + n0 + qd * 8) = v;
-  }
 }
 
 }  // namespace decode

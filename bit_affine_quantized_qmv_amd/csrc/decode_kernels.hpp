@@ -20,29 +20,17 @@ constexpr int kChunkTiles = 2;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kChunkXBytes = 64 * 1024;
 
-#ifndef QMM_STREAM_WAVES
-#define QMM_STREAM_WAVES 8
-#endif
-#ifndef QMM_STREAM_MIN_WG
-#define QMM_STREAM_MIN_WG 2
-#endif
-constexpr int kStreamWaves = QMM_STREAM_WAVES;
+// Eight waves per workgroup, two per SIMD (the kernels' register budget is 256): more waves
+// per workgroup or per SIMD measured slower on the lm_head weight.
+constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
-#ifndef QMM_PAIR
-#define QMM_PAIR 2
-#endif
-constexpr int kPair = QMM_PAIR;   // weight tiles consumed together per slot
-#ifndef QMM_RING_FACTOR
-#define QMM_RING_FACTOR 2
-#endif
-constexpr int kRingFactor = QMM_RING_FACTOR;   // sub-blocks of weight loads in flight
-#ifndef QMM_Y_LDS
-#define QMM_Y_LDS 0
-#endif
-constexpr bool kYLds = QMM_Y_LDS != 0;   // full tile pairs stored through LDS
+constexpr int kStreamWavesPerSimd = 2;
+constexpr int kPair = 2;         // weight tiles consumed together per slot
+constexpr int kRingFactor = 2;   // sub-blocks of weight loads in flight
+constexpr int kMaxWgPerCu = 8;   // cap on resident workgroups per compute unit in the grid size
 
 template <class T, int BITS, int GS, int MT, int D, bool SBB>
-__global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_kernel(const MatArgs a,
+__global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_stream_kernel(const MatArgs a,
                                                                                      const int pairs_base,
                                                                                      const int pairs_rem) {
   // The slots of a wave's tile pairs form one stream, consumed in sub-blocks of D slots (D
@@ -62,7 +50,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   constexpr int R = RF * D;
   // one bias MFMA per two slots (the launcher picks D >= 2 exactly when the slots per row
   // are even, which is when bias_span gives 2)
-  constexpr bool kPairBias = QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && D >= 2;
+  constexpr bool kPairBias = GS >= 64 && D >= 2;
   constexpr bool kBuf = BITS == 4 || BITS == 8;
   static_assert(!SBB || kBuf, "block scale/bias loads use the buffer path");
   constexpr int NHB = D * S::kGroups;   // scale (or bias) halfwords per tile row per sub-block
@@ -109,12 +97,10 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
   const int64_t t_end = p_end * TN < n_tiles ? p_end * TN : n_tiles;
   const int nit = Kp / S::kSpan;             // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
-  uint16_t* ys = (uint16_t*)(sxs + (K / GS + kSxPad) * MROWS) + wave * MROWS * kYRow;
-  // fused argmax: per-row keys of the workgroup, after the store staging area
-  unsigned long long* kl = (unsigned long long*)(ys - wave * MROWS * kYRow + (kYLds ? kStreamWaves * MROWS * kYRow : 0));
+  // fused argmax: per-row keys of the workgroup, after the activation sums
+  unsigned long long* kl = (unsigned long long*)(sxs + (K / GS + kSxPad) * MROWS);
   const bool do_argmax = a.argmax_keys != nullptr;
   const bool store_y = a.y != nullptr;
-  const bool y_vec = (N & 7) == 0 && ((uintptr_t)yb & 15) == 0;
 
   int gword = 0;
   uint32_t gshift = 0;
@@ -220,16 +206,13 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-#ifndef QMM_EARLY_W
-#define QMM_EARLY_W 2
-#endif
-  if (QMM_EARLY_W && nbatch == 1) {
+  if (nbatch == 1) {
     // activation loads first, the weight prefetch right behind them (loads return in issue
     // order, so waiting for the activations does not wait for the weights)
     XStage<MROWS> st;
     stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows);
     // every wave's activation loads are issued before any weight load enters the queue
-    if (QMM_EARLY_W >= 2) lds_barrier();
+    lds_barrier();
     prefetch();
     stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
     zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
@@ -343,14 +326,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_stream_
           argmax_update<T, MT>(best, acc[t], n, c_p + t < t_end && n < N);
         }
       }
-      bool stored = !store_y;
-      if constexpr (kYLds && TN == 2) {
-        if (!stored && y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
-          store_pair_lds<T, MT, TN>(acc, ys, yb, rows, c_p * 16, N, lane, lg, col);
-          stored = true;
-        }
-      }
-      if (!stored) {
+      if (store_y) {
 #pragma unroll
         for (int t = 0; t < TN; ++t)
           if (c_p + t < t_end) store_tile<T, MT>(acc[t], yb, rows, (c_p + t) * 16 + col, N, lg);
@@ -558,10 +534,7 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
   if (occ != hipSuccess) return occ;
   // one full wave of workgroups (every CU at its occupancy), tile pairs spread over all waves
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
-#ifndef QMM_MAX_WG_PER_CU
-#define QMM_MAX_WG_PER_CU 8
-#endif
-  const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
+  const int64_t full = (int64_t)device_cus() * std::min(per_cu, kMaxWgPerCu);
   const int64_t blocks = std::min<int64_t>(full, (n_pairs + kStreamWaves - 1) / kStreamWaves);
   const int64_t waves_total = blocks * kStreamWaves;
   if (n_pairs / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -583,19 +556,11 @@ hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
   return launch_stream_sb<T, BITS, GS, MT, D, false>(a, stream, lds);
 }
 
-// Slots per main-loop block: the largest of 8, 4, 2, 1 dividing the slots per tile.
+// Slots per main-loop block (block_slots): 2 when the slots per tile are even, else 1.
 template <class T, int BITS, int GS, int MT>
 hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
   const int nit = (int)((a.K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
-#ifndef QMM_MAX_BLOCK_SLOTS
-#define QMM_MAX_BLOCK_SLOTS 2
-#endif
-  if constexpr (QMM_MAX_BLOCK_SLOTS >= 8)
-    if (nit % 8 == 0) return launch_stream_d<T, BITS, GS, MT, 8>(a, stream, lds);
-  if constexpr (QMM_MAX_BLOCK_SLOTS >= 4)
-    if (nit % 4 == 0) return launch_stream_d<T, BITS, GS, MT, 4>(a, stream, lds);
-  if constexpr (QMM_MAX_BLOCK_SLOTS >= 2)
-    if (nit % 2 == 0) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
+  if (block_slots(nit) == 2) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
   return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
 }
 
@@ -607,7 +572,7 @@ hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P,
   if (occ != hipSuccess) return occ;
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
   const int64_t groups = kStreamWaves / P;
-  const int64_t full = (int64_t)device_cus() * std::min(per_cu, QMM_MAX_WG_PER_CU);
+  const int64_t full = (int64_t)device_cus() * std::min(per_cu, kMaxWgPerCu);
   const int64_t blocks = std::min<int64_t>(full, (n_pairs + groups - 1) / groups);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a, P,
                      spp);
@@ -650,8 +615,7 @@ hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
 template <int BITS, int MT, int GS>
 constexpr int stream_lds_bytes(int K) {
   const int Kp = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan * Slot<BITS, GS>::kSpan;
-  return 16 * MT * Kp * 2 + (K / GS + kSxPad) * 16 * MT * 4 + (kYLds ? kStreamWaves * 16 * MT * kYRow * 2 : 0) +
-         16 * MT * 8;
+  return 16 * MT * Kp * 2 + (K / GS + kSxPad) * 16 * MT * 4 + 16 * MT * 8;
 }
 
 template <class T, int BITS, int GS>

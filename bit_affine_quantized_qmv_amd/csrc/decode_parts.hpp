@@ -7,7 +7,7 @@ namespace qmm {
 namespace decode {
 
 template <class T, int BITS, int GS, int MT, int D, bool SBB>
-__global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_parts_kernel(const MatArgs a, const int P,
+__global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts_kernel(const MatArgs a, const int P,
                                                                                     const int spp) {
   // The workgroup's waves form G = 8/P groups of P waves.  Round r: group g works on tile
   // pair wg_p0 + r*G + g of the workgroup's pair range, wave j of the group on slots
@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kStreamThreads, QMM_STREAM_MIN_WG) void qmv_parts_k
   constexpr int TN = kPair;
   constexpr int RF = kRingFactor;
   constexpr int R = RF * D;
-  constexpr bool kPairBias = QMM_MAX_BLOCK_SLOTS >= 2 && GS >= 64 && D >= 2;
+  constexpr bool kPairBias = GS >= 64 && D >= 2;
   constexpr bool kBuf = BITS == 4 || BITS == 8;
   static_assert(!SBB || kBuf, "block scale/bias loads use the buffer path");
   constexpr int NHB = D * S::kGroups;

@@ -272,8 +272,10 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
 // per (chunk, row).  Each writes its chunk's k largest words (zero words past a short
 // chunk) to the workspace, then counts itself done on the row's counter; the row's last
 // workgroup sorts the parts * k words (at most kCand) and writes the row's result, then
-// clears the counter.  Candidate words travel through device-scope atomic stores and loads;
-// each writer waits for its stores to complete before its workgroup is counted.
+// clears the counter.  Ordering: every writer thread's words are ordered before its
+// workgroup's count by a release fence at device scope and the workgroup barrier; the count
+// is an acquire-release read-modify-write; the last workgroup's threads issue an acquire
+// fence at device scope before reading the words.
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, const int parts, const int64_t chunk) {
   __shared__ TopkSmem sm;
@@ -292,16 +294,15 @@ __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, 
   });
   for (uint32_t j = kk + threadIdx.x; j < k; j += kThreads)   // a chunk shorter than k
     __hip_atomic_store(&words[j], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // The words are device-scope atomic stores; once this thread's stores have completed
-  // (vmcnt 0) they are visible device-wide, before the workgroup counts itself done.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned done = __hip_atomic_fetch_add(&counters[2 * r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned done = __hip_atomic_fetch_add(&counters[2 * r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = done + 1u == (unsigned)parts ? 1u : 0u;
   }
   __syncthreads();
   if (sm.last == 0u) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const unsigned long long* row_words = (const unsigned long long*)a.workspace + kTopkWsHeader * a.rows + r * parts * (int64_t)k;
   const uint32_t m = (uint32_t)parts * k;
   for (uint32_t j = threadIdx.x; j < m; j += kThreads)
