@@ -447,26 +447,37 @@ __device__ inline int bias_span(int slots_per_row) {
   return (GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
 }
 
-// Parts per row: the largest power of two <= min(8, slots/8), at least 1 (rows of at most
-// 15 slots are not cut).  A function of K, the code width and the group size only, so every
-// decode kernel sums a row the same way: part sums in k order, then added part by part.
-template <int BITS, int GS>
-__host__ __device__ inline int row_parts(int64_t K) {
-  const int64_t nit = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan;
-  int p = 1;
-  while (p < 8 && 2 * p * 8 <= nit) p *= 2;
-  return p;
+// Parts per row, a function of K, the weight's row count (N, times the experts of a gathered
+// stack), the code width and the group size only, so every decode kernel sums a row the same
+// way (part sums in k order, then added part by part) for every row count and plan of a call
+// on that weight.  Matrices of kFewRowsN rows or more:
+// the largest power of two <= min(8, slots/8), at least 1 (rows of at most 15 slots are not
+// cut).  Fewer rows (fewer tile pairs than two per compute unit): the largest power of two
+// <= min(8, slots / block_slots), so each wave walks as few slots as possible and the row's
+// latency shrinks (one 16-row tile of a K = 1024, 4-bit weight: 4 parts of 2 slots).
+constexpr int64_t kFewRowsN = 16384;
+
+// Rows of the weight a call reads from: N, or N per expert times the experts of a stack.
+__host__ __device__ inline int64_t weight_rows(const MatArgs& a) {
+  return a.w_index ? a.N * a.num_experts : a.N;
 }
 
 // Sub-block size (slots) the decode kernels use for a row of nit slots.
 __host__ __device__ inline int block_slots(int nit) { return nit % 2 == 0 ? 2 : 1; }
 
-// Slots per part: the slots rounded up to a multiple of P * D, divided by P (a part may
-// reach past the row's last slot; those slots add nothing).
 template <int BITS, int GS>
-__host__ __device__ inline int part_slots(int64_t K) {
+__host__ __device__ inline int row_parts(int64_t K, int64_t N) {
+  const int64_t nit = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan;
+  const int step = N < kFewRowsN ? block_slots((int)nit) : 8;
+  int p = 1;
+  while (p < 8 && 2 * p * step <= nit) p *= 2;
+  return p;
+}
+
+template <int BITS, int GS>
+__host__ __device__ inline int part_slots(int64_t K, int64_t N) {
   const int nit = (int)((K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
-  const int p = row_parts<BITS, GS>(K), d = block_slots(nit);
+  const int p = row_parts<BITS, GS>(K, N), d = block_slots(nit);
   return (nit + p * d - 1) / (p * d) * d;
 }
 
@@ -579,15 +590,15 @@ __device__ inline void argmax_publish(unsigned long long* key, unsigned long lon
 }
 
 // Completion of the fused argmax inside the decode kernel.  Every thread's key merges
-// (argmax_publish) are ordered before its workgroup counts itself done by a release fence at
-// device scope and the workgroup barrier; the count is an acquire-release read-modify-write;
-// the last workgroup to count issues an acquire fence at device scope in every thread before
-// it reads the keys.  That workgroup turns each row's key into (index, value) and sets the
+// (argmax_publish) happen before the workgroup barrier, which happens before thread 0's count;
+// the count is an acquire-release read-modify-write at device scope, whose release half orders
+// the whole workgroup's merges before it (one L2 write-back per workgroup rather than one per
+// wave); the last workgroup to count issues an acquire fence at device scope in every thread
+// before it reads the keys.  That workgroup turns each row's key into (index, value) and sets the
 // keys and the counter back to zero, so the workspace is all-zero again when the kernel
 // ends.  `last` is a workgroup-shared word that is free once every thread has arrived here
 // (it is first written after the barrier below).  Called by every thread.
 __device__ inline void argmax_complete(const MatArgs& a, int64_t total_rows, unsigned* last) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned wgs = gridDim.x * gridDim.y * gridDim.z;

@@ -417,8 +417,8 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
 
   const int nit_total = (K + S::kSpan - 1) / S::kSpan;   // the last slot may end past K
   // rows cut into parts (see row_parts): part sums added in part order, as the parts kernel does
-  const int n_parts = row_parts<BITS, GS>(K);
-  const int spp = part_slots<BITS, GS>(K);
+  const int n_parts = row_parts<BITS, GS>(K, weight_rows(a));
+  const int spp = part_slots<BITS, GS>(K, weight_rows(a));
   bool have_total = false;
   f32x4 total[TN][MT];
   const bool pair_bias = bias_span<GS>(nit_total) == 2;
@@ -581,8 +581,8 @@ hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P,
 
 template <class T, int BITS, int GS, int MT>
 hipError_t launch_parts(const MatArgs& a, hipStream_t stream, int lds) {
-  const int P = row_parts<BITS, GS>(a.K);
-  const int spp = part_slots<BITS, GS>(a.K);
+  const int P = row_parts<BITS, GS>(a.K, weight_rows(a));
+  const int spp = part_slots<BITS, GS>(a.K, weight_rows(a));
   const int nit = (int)((a.K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
   if (block_slots(nit) == 2) {
     if constexpr (BITS == 4 || BITS == 8) {
@@ -622,7 +622,7 @@ template <class T, int BITS, int GS>
 hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   const int K = (int)a.K;
   // long rows (see row_parts) run the parts kernel, the others the streaming kernel
-  const bool parts = row_parts<BITS, GS>(K) > 1;
+  const bool parts = row_parts<BITS, GS>(K, weight_rows(a)) > 1;
   const int lds1 = parts ? parts_lds_bytes<1, GS, BITS>(K) : stream_lds_bytes<BITS, 1, GS>(K);
   const int lds2 = parts ? parts_lds_bytes<2, GS, BITS>(K) : stream_lds_bytes<BITS, 2, GS>(K);
   auto run1 = [&](const MatArgs& m) {

@@ -272,10 +272,11 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
 // per (chunk, row).  Each writes its chunk's k largest words (zero words past a short
 // chunk) to the workspace, then counts itself done on the row's counter; the row's last
 // workgroup sorts the parts * k words (at most kCand) and writes the row's result, then
-// clears the counter.  Ordering: every writer thread's words are ordered before its
-// workgroup's count by a release fence at device scope and the workgroup barrier; the count
-// is an acquire-release read-modify-write; the last workgroup's threads issue an acquire
-// fence at device scope before reading the words.
+// clears the counter.  Ordering: every writer thread's words happen before the workgroup
+// barrier, which happens before thread 0's count; the count is an acquire-release
+// read-modify-write at device scope whose release half orders the workgroup's words before
+// it; the last workgroup's threads issue an acquire fence at device scope before reading the
+// words.
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, const int parts, const int64_t chunk) {
   __shared__ TopkSmem sm;
@@ -294,7 +295,6 @@ __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, 
   });
   for (uint32_t j = kk + threadIdx.x; j < k; j += kThreads)   // a chunk shorter than k
     __hip_atomic_store(&words[j], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned done = __hip_atomic_fetch_add(&counters[2 * r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
