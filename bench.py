@@ -454,6 +454,9 @@ def main():
         line["context"]["forced_vs_folded"] = _paired_ratio(
             args, q, torch, lambda i: q.qmv(xs[i % copies], qws[i % copies], out=ys[i % copies]),
             lambda i: q.qmv(xs[i % copies], qws[i % copies], q.QMM_FLAG_FORCE_STRIDED, out=ys[i % copies]))
+        # its HBM reads from the committed FETCH_SIZE pass (null once the kernel source changed)
+        line["context"]["forced_vs_folded"]["fetch_ratio_to_folded"] = _profile_field(
+            "qmv_stream_kernel_forced_per_batch_element_fetch.md", "forced-json", QMV_SOURCES, "ratio_to_folded")
         # the same weight at one activation row
         x1 = [synth.normal_x((1, k), cfg["dtype"], seed=cfg["x_seed"]).to(dev) for _ in range(copies)]
         y1 = [torch.empty(1, n, dtype=x0.dtype, device=dev) for _ in range(copies)]

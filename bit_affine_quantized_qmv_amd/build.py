@@ -30,6 +30,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Test helper built beside the library: fills and reads back LDS between library kernels.
+TEST_HELPER_SRC = os.path.join(ROOT, "tests", "lds_fill.hip")
+TEST_HELPER_LIB = os.path.join(ROOT, "tests", "_lds_fill.so")
+
+
+def build_test_helper(verbose: bool = True) -> str:
+    tmp = TEST_HELPER_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-x", "hip", "-shared", TEST_HELPER_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for the test helper:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, TEST_HELPER_LIB)
+    if verbose:
+        print("built", TEST_HELPER_LIB)
+    return TEST_HELPER_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
@@ -42,6 +59,7 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_test_helper(verbose)
     return LIB
 
 
