@@ -500,7 +500,7 @@ def main():
         tbytes = qmv_bytes + m * n * 2 + m * tk * 8
         topk_rows = {"qmv_topk": _leg(
             "decode + top-k effective HBM GB/s", tbytes, tt, "hbm", "GB/s", HBM_PEAK_GBS,
-            "qmv_stream_kernel + topk_parts_kernel",
+            "qmv_stream_kernel + topk_select_kernel + topk_merge_kernel",
             {"workload": "lm_head decode qmv + per-row top-50: x [32,1,1024] bf16, W [151936,1024] 4-bit "
                          "group 64; logits stored, then read by the top-k pass",
              "algorithmic_bytes_per_call": tbytes})}
@@ -509,7 +509,7 @@ def main():
                          nsteps, nwarm, torch, not args.no_graph)
         obytes = m * n * 2 + m * tk * 8
         topk_rows["topk_alone"] = _leg(
-            "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_parts_kernel",
+            "top-k effective HBM GB/s", obytes, to, "hbm", "GB/s", HBM_PEAK_GBS, "topk_select_kernel + topk_merge_kernel",
             {"workload": "per-row top-50 of [32,151936] bf16 logits (column chunks per row)",
              "algorithmic_bytes_per_call": obytes})
         out["next"]["topk"] = topk_rows

@@ -218,9 +218,9 @@ def _dtype_code(dtype) -> int:
 
 
 def topk_workspace(rows: int, device) -> torch.Tensor:
-    """A zeroed workspace for qmm_topk / qmm_qmv_topk over `rows` rows (reusable in stream
-    order: the kernels leave it zero)."""
-    return torch.zeros((32776 * max(rows, 1) + 7) // 8, dtype=torch.int64, device=device)
+    """A workspace for qmm_topk / qmm_qmv_topk over `rows` rows (reusable in stream order;
+    its content does not matter)."""
+    return torch.empty((32776 * max(rows, 1) + 7) // 8, dtype=torch.int64, device=device)
 
 
 def topk(logits: torch.Tensor, k: int, out_index=None, out_value=None, workspace=None, split=True):

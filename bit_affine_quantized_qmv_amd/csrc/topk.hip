@@ -5,23 +5,30 @@
 // to token 0; keeping per-row candidates instead of whole logit rows is what a sharded
 // lm_head exchanges).
 //
-// A 1024-thread workgroup per row (or per column chunk of a row), over the row's 16-bit
-// values mapped to order keys (unsigned, larger key = larger value), read 8 at a time when
-// the row is 16-byte aligned:
-//   1. histogram of the key's high 11 bits (2048 bins, so that the values of a typical
-//      logit row spread over many LDS counters) -> the bin that holds the k-th largest key,
-//      found with a block-wide suffix count;
-//   2. usual case, at most 4096 keys in that bin and above: all of them are the candidates;
+// Each workgroup selects from one span of columns (a whole row, or one column chunk of it),
+// over the 16-bit values mapped to order keys (unsigned, larger key = larger value):
+//   0. spans of up to 8 * threads * 4 columns are loaded once into registers (8 consecutive
+//      columns per run, one 16-byte load when the row is 16-byte aligned, two keys per
+//      register); longer spans are read from global memory on each pass;
+//   1. with the keys in registers, a histogram of each thread's largest key over the key's
+//      high 11 bits gives a bin B that at least k of those maxima reach, so the k largest
+//      keys all lie in bin B or above; when those keys fit the candidate buffer (4096
+//      words, the usual case) they are the candidates;
+//   2. otherwise, a histogram of every key's high 11 bits (2048 bins, so that the values of
+//      a typical logit row spread over many LDS counters) -> the bin that holds the k-th
+//      largest key, found with a block-wide suffix count; at most 4096 keys in that bin and
+//      above: all of them are the candidates;
 //   3. otherwise, a histogram of the low 5 bits inside that bin gives the k-th largest key
 //      itself (t) and the number of keys above it (g < k); the g keys above t are the
 //      candidates [0, g) in any order, and the first k - g keys equal to t in column order
 //      (a block-wide prefix count over consecutive column runs) are [g, k).
-// The candidates, as (key << 32 | ~column) words, are ranked: up to 512 by counting the
-// larger words, more by a bitonic sort in LDS; the first k are written out.  With a
-// workspace, long rows are cut into column chunks handled by workgroups of their own
-// (enough for about one workgroup per compute unit); the row's last workgroup ranks the
-// chunks' candidates.  The result does not depend on the order in which threads or
-// workgroups run.
+// The candidates, as (key << 32 | ~column) words, are ranked: while there are at most as
+// many as threads by counting the larger words, beyond that by a bitonic sort in LDS; the
+// first k are the span's result.  With a workspace, long rows are cut into column chunks
+// (about one workgroup per compute unit in all): a select kernel writes each chunk's k
+// best words to the workspace, and a merge kernel, one workgroup per row, ranks the row's
+// parts * k words.  The kernel boundary orders the two, so no workgroup waits for another.
+// The result does not depend on the order in which threads or workgroups run.
 #include <climits>
 
 #include "device_common.hpp"
@@ -31,10 +38,19 @@
 namespace qmm {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kRun = 8;   // consecutive columns per thread in the collecting pass
-constexpr int kCand = 4096;   // candidates the one-pass collection takes
+constexpr int kRowThreads = 1024;     // one workgroup per whole row
+constexpr int kSelThreads = 1024;     // one workgroup per column chunk of a row
+constexpr int kMergeThreads = 1024;   // one workgroup per row, merging its chunks' words
+constexpr int kRun = 8;               // consecutive columns per thread and step
+constexpr int kSelRuns = 4;           // 8-column runs per thread held in registers: chunks
+constexpr int kRowRuns = 4;           // ... and whole rows (up to 32768 columns)
+constexpr int kCand = 4096;           // candidates the one-pass collection takes
+constexpr int kTargetWorkgroups = 256;   // chunk workgroups over all rows: about one per CU
+constexpr int64_t kMinChunk = 2048;      // columns per chunk, at least
+
+// Columns a workgroup of THREADS threads holds in registers at RUNS runs per thread.
+template <int THREADS, int RUNS>
+constexpr int64_t reg_cols() { return (int64_t)THREADS * kRun * RUNS; }
 
 template <bool FP16>
 __device__ inline uint32_t order_key(uint32_t b) {
@@ -47,7 +63,9 @@ __device__ inline uint32_t order_key(uint32_t b) {
 __device__ inline uint32_t key_bits(uint32_t o) { return (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu); }
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets the sum.
+template <int THREADS>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sums, uint32_t* total) {
+  constexpr int kWaves = THREADS / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t s = v;
 #pragma unroll
@@ -73,46 +91,143 @@ constexpr int kHiShift = 5;
 constexpr int kHiBins = 1 << (16 - kHiShift);
 constexpr int kLoBins = 1 << kHiShift;
 
-// Calls f(column, key) for every column of the row; each thread takes 8 consecutive
-// columns per step (one 16-byte load when the row is 16-byte aligned).
-template <bool FP16, class F>
-__device__ inline void for_each_key(const uint16_t* row, int64_t n, F&& f) {
-  const bool vec = ((uintptr_t)row & 15u) == 0u;
-  const int64_t n8 = vec ? (n & ~(int64_t)7) : 0;
-  for (int64_t i = (int64_t)threadIdx.x * 8; i < n8; i += (int64_t)kThreads * 8) {
-    const u32x4 v = *(const u32x4*)(row + i);
+// The order keys of columns [i0, i0 + 8) of a span of len columns (0 past its end; real keys
+// are never 0): one 16-byte load when the span is 16-byte aligned and the run is whole.
+template <bool FP16>
+__device__ inline void load_run(const uint16_t* row, int64_t i0, int64_t len, bool vec, uint32_t (&o)[kRun]) {
+  if (vec && i0 + kRun <= len) {
+    const u32x4 v = *(const u32x4*)(row + i0);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      f(i + 2 * e, order_key<FP16>(w[e] & 0xFFFFu));
-      f(i + 2 * e + 1, order_key<FP16>(w[e] >> 16));
+      o[2 * e] = order_key<FP16>(w[e] & 0xFFFFu);
+      o[2 * e + 1] = order_key<FP16>(w[e] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) o[e] = i0 + e < len ? order_key<FP16>(row[i0 + e]) : 0u;
+  }
+}
+
+// Keys of a span read from global memory on every pass.  Step j of thread t covers columns
+// 8 * (t + THREADS * j) .. + 7.
+template <bool FP16, int THREADS>
+struct GlobalKeys {
+  static constexpr bool kHeldKeys = false;   // no cheap per-thread maximum (a pass of its own)
+  const uint16_t* row;
+  int64_t len;
+  __device__ uint32_t max_key() const { return 0u; }
+  // f(column in span, key) for every column
+  template <class F>
+  __device__ void each(F&& f) const {
+    const bool vec = ((uintptr_t)row & 15u) == 0u;
+    for (int64_t i0 = (int64_t)threadIdx.x * kRun; i0 < len; i0 += (int64_t)THREADS * kRun) {
+      uint32_t o[kRun];
+      load_run<FP16>(row, i0, len, vec, o);
+#pragma unroll
+      for (int e = 0; e < kRun; ++e)
+        if (o[e]) f(i0 + e, o[e]);
     }
   }
-  for (int64_t i = n8 + threadIdx.x; i < n; i += kThreads) f(i, order_key<FP16>(row[i]));
-}
+  // f(first column, keys of the run) for every step, the same number of calls in every thread
+  template <class F>
+  __device__ void steps(F&& f) const {
+    const bool vec = ((uintptr_t)row & 15u) == 0u;
+    for (int64_t base = 0; base < len; base += (int64_t)THREADS * kRun) {
+      const int64_t i0 = base + (int64_t)threadIdx.x * kRun;
+      uint32_t o[kRun];
+      load_run<FP16>(row, i0, len, vec, o);
+      f(i0, o);
+    }
+  }
+};
+
+// Keys of a span of at most reg_cols<THREADS, RUNS>() columns, loaded once into registers
+// with the same column assignment (run j of thread t: columns 8 * (t + THREADS * j) .. + 7),
+// two 16-bit keys per register (column 2e in the low half, 2e + 1 in the high half).
+template <bool FP16, int THREADS, int RUNS>
+struct RegKeys {
+  static constexpr bool kHeldKeys = true;
+  uint32_t p[RUNS][4];
+  __device__ __forceinline__ static uint32_t pack(uint32_t w) {
+    return order_key<FP16>(w & 0xFFFFu) | (order_key<FP16>(w >> 16) << 16);
+  }
+  __device__ __forceinline__ void load(const uint16_t* row, int64_t len) {
+    const bool vec = ((uintptr_t)row & 15u) == 0u;
+    bool whole[RUNS];
+    // every whole run's load is issued before any key is formed
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j) {
+      const int64_t i0 = (int64_t)kRun * (threadIdx.x + THREADS * j);
+      whole[j] = vec && i0 + kRun <= len;
+      if (whole[j]) {
+        const u32x4 v = *(const u32x4*)(row + i0);
+        p[j][0] = v.x;
+        p[j][1] = v.y;
+        p[j][2] = v.z;
+        p[j][3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j) {
+      const int64_t i0 = (int64_t)kRun * (threadIdx.x + THREADS * j);
+      if (whole[j]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[j][e] = pack(p[j][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t c = i0 + 2 * e;
+          const uint32_t lo = c < len ? order_key<FP16>(row[c]) : 0u;
+          const uint32_t hi = c + 1 < len ? order_key<FP16>(row[c + 1]) : 0u;
+          p[j][e] = lo | (hi << 16);
+        }
+      }
+    }
+  }
+  // the thread's largest key (0 when it holds none)
+  __device__ __forceinline__ uint32_t max_key() const {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, max(p[j][e] & 0xFFFFu, p[j][e] >> 16));
+    return m;
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t o = (p[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        if (o) f((int64_t)kRun * (threadIdx.x + THREADS * j) + e, o);
+      }
+  }
+};
 
 // Workgroup-shared state of one selection.
 struct TopkSmem {
   uint32_t hist[kHiBins];
-  uint32_t wave_sums[kWaves];
+  uint32_t wave_sums[16];
   uint32_t sel[4];
   uint32_t slot;
-  uint32_t last;
   unsigned long long cand[kCand];
 };
 
 // Sorts the m words cand[0, m) (m <= kCand) ascending, padded to a power of two mp with
 // zero words (below every candidate), and returns mp: cand[mp - 1 - j] is the j-th largest.
+template <int THREADS>
 __device__ inline uint32_t sort_words(unsigned long long* cand, uint32_t m) {
   const uint32_t tid = threadIdx.x;
   uint32_t mp = 1u;
   while (mp < m) mp <<= 1;
   __syncthreads();
-  for (uint32_t j = m + tid; j < mp; j += kThreads) cand[j] = 0ull;
+  for (uint32_t j = m + tid; j < mp; j += THREADS) cand[j] = 0ull;
   for (uint32_t size = 2u; size <= mp; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1) {
       __syncthreads();
-      for (uint32_t i = tid; i < mp; i += kThreads) {
+      for (uint32_t i = tid; i < mp; i += THREADS) {
         const uint32_t j = i ^ stride;
         if (j > i) {
           const unsigned long long x = cand[i], y = cand[j];
@@ -137,65 +252,120 @@ __device__ inline void store_word(unsigned long long w, uint32_t j, uint32_t k, 
 }
 
 // Calls f(j, word) for the j-th largest of the m distinct words cand[0, m), j < kk.  Up to
-// 512 words each thread ranks one word by counting the larger ones (no barriers); beyond
-// that the words are sorted.
-constexpr uint32_t kRankMax = 512;
-template <class F>
+// THREADS words each thread ranks one word by counting the larger ones (no barriers);
+// beyond that the words are sorted.
+template <int THREADS, class F>
 __device__ inline void emit_largest(unsigned long long* cand, uint32_t m, uint32_t kk, F&& f) {
-  if (m <= kRankMax) {
+  if (m <= (uint32_t)THREADS) {
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < m; i += kThreads) {
+    const uint32_t i = threadIdx.x;
+    if (i < m) {
       const unsigned long long w = cand[i];
-      uint32_t r = 0u;
-      for (uint32_t j = 0; j < m; ++j) r += cand[j] > w ? 1u : 0u;
+      uint32_t r = 0u, j = 0u;
+      for (; j + 8u <= m; j += 8u) {   // eight words read at once, then compared
+        unsigned long long c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cand[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += c[u] > w ? 1u : 0u;
+      }
+      for (; j < m; ++j) r += cand[j] > w ? 1u : 0u;
       if (r < kk) f(r, w);
     }
     return;
   }
-  const uint32_t mp = sort_words(cand, m);
-  for (uint32_t j = threadIdx.x; j < kk; j += kThreads) f(j, cand[mp - 1u - j]);
+  const uint32_t mp = sort_words<THREADS>(cand, m);
+  for (uint32_t j = threadIdx.x; j < kk; j += THREADS) f(j, cand[mp - 1u - j]);
 }
 
-// Collects candidate (key << 32 | ~column) words of columns [col0, col0 + len) of a row into
-// cand and returns their number m >= kk; the kk largest of them are the kk largest of the
-// columns.  `row` points at column col0.
-template <bool FP16>
-__device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t col0, int64_t len, uint32_t kk, TopkSmem& sm) {
+// From the per-bin counts in sm.hist, the bin where the count from the top reaches k:
+// sm.sel[0] = that bin, sm.sel[1] = count in the bins above it, sm.sel[2] = count in it and
+// above; sm.sel[2] stays below k when the counts total less than k.  Also zeroes sm.slot.
+template <int THREADS>
+__device__ inline void find_bin(uint32_t k, TopkSmem& sm) {
+  const int tid = threadIdx.x;
+  constexpr int kPer = kHiBins / THREADS;   // bins per thread, thread 0 holding the top ones
+  static_assert(kPer * THREADS == kHiBins, "whole bins per thread");
+  if (tid == 0) {
+    sm.sel[2] = 0u;
+    sm.slot = 0u;
+  }
+  uint32_t c[kPer], sum = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = sm.hist[kHiBins - 1 - kPer * tid - j];
+    sum += c[j];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan<THREADS>(sum, sm.wave_sums, &total);   // barriers inside
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (run < k && run + c[j] >= k) {
+      sm.sel[0] = (uint32_t)(kHiBins - 1 - kPer * tid - j);
+      sm.sel[1] = run;
+      sm.sel[2] = run + c[j];
+    }
+    run += c[j];
+  }
+  __syncthreads();
+}
+
+// Collects candidate (key << 32 | ~column) words of the span [col0, col0 + len) of a row,
+// whose keys come from ks (the exact-threshold pass, rare, reads them from gk in column
+// order), into cand and returns their number m >= kk; the kk largest of them are the kk
+// largest of the span.
+template <bool FP16, int THREADS, class KS>
+__device__ __forceinline__ uint32_t select_words(const KS& ks, const GlobalKeys<FP16, THREADS>& gk, int64_t col0,
+                                                 uint32_t kk, TopkSmem& sm) {
   const int tid = threadIdx.x;
   const uint32_t k = kk;
   auto word = [&](uint32_t o, int64_t i) {
     return ((unsigned long long)o << 32) | (0xFFFFFFFFu - (uint32_t)(col0 + i));
   };
 
-  // 1. histogram of the high bits; the bin of the k-th largest key by a suffix count
-  for (int b = tid; b < kHiBins; b += kThreads) sm.hist[b] = 0u;
-  __syncthreads();
-  for_each_key<FP16>(row, len, [&](int64_t, uint32_t o) { atomicAdd(&sm.hist[o >> kHiShift], 1u); });
-  __syncthreads();
-  {
-    static_assert(kHiBins == 2 * kThreads, "two bins per thread");
-    const int b_hi = kHiBins - 1 - 2 * tid, b_lo = b_hi - 1;   // thread 0 holds the top bins
-    const uint32_t c_hi = sm.hist[b_hi], c_lo = sm.hist[b_lo];
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan(c_hi + c_lo, sm.wave_sums, &total);
-    if (above < k && above + c_hi >= k) {
-      sm.sel[0] = (uint32_t)b_hi;
-      sm.sel[1] = above;
-      sm.sel[2] = above + c_hi;
-    } else if (above + c_hi < k && above + c_hi + c_lo >= k) {
-      sm.sel[0] = (uint32_t)b_lo;
-      sm.sel[1] = above + c_hi;
-      sm.sel[2] = above + c_hi + c_lo;
+  if constexpr (KS::kHeldKeys) {
+    // 0. A threshold from each thread's largest key: if the bin of the k-th largest of these
+    // maxima is B, at least k keys (those maxima, one per thread) lie in bin B or above, so
+    // the k largest keys do too.  One histogram update per thread instead of one per key;
+    // taken when the keys in bin B or above fit the candidate buffer (the usual case).
+    for (int b = tid; b < kHiBins; b += THREADS) sm.hist[b] = 0u;
+    __syncthreads();
+    const uint32_t mx = ks.max_key();
+    if (mx) atomicAdd(&sm.hist[mx >> kHiShift], 1u);
+    __syncthreads();
+    find_bin<THREADS>(k, sm);
+    if (sm.sel[2] >= k) {
+      // each thread counts its candidates, reserves that many slots with one atomic, and
+      // writes them there
+      const uint32_t lo_bin = sm.sel[0];
+      uint32_t cnt = 0u;
+      ks.each([&](int64_t, uint32_t o) { cnt += (o >> kHiShift) >= lo_bin ? 1u : 0u; });
+      uint32_t j = cnt ? atomicAdd(&sm.slot, cnt) : 0u;
+      ks.each([&](int64_t i, uint32_t o) {
+        if ((o >> kHiShift) >= lo_bin) {
+          if (j < (uint32_t)kCand) sm.cand[j] = word(o, i);
+          ++j;
+        }
+      });
+      __syncthreads();
+      const uint32_t m = sm.slot;
+      if (m <= (uint32_t)kCand) return m;
+      __syncthreads();   // every thread has read sm.slot before the histogram pass resets it
     }
-    if (tid == 0) sm.slot = 0u;
   }
+
+  // 1. histogram of the high bits; the bin of the k-th largest key by a suffix count
+  for (int b = tid; b < kHiBins; b += THREADS) sm.hist[b] = 0u;
   __syncthreads();
+  ks.each([&](int64_t, uint32_t o) { atomicAdd(&sm.hist[o >> kHiShift], 1u); });
+  __syncthreads();
+  find_bin<THREADS>(k, sm);
   const uint32_t hi = sm.sel[0];
   const uint32_t n_ge = sm.sel[2];   // keys in bin hi or above
   if (n_ge <= (uint32_t)kCand) {
     // Usual case: every key in bin hi or above is a candidate (collected in any order; the
-    // word carries the column), then sort them all.
-    for_each_key<FP16>(row, len, [&](int64_t i, uint32_t o) {
+    // word carries the column).
+    ks.each([&](int64_t i, uint32_t o) {
       if ((o >> kHiShift) >= hi) sm.cand[atomicAdd(&sm.slot, 1u)] = word(o, i);
     });
     return n_ge;
@@ -204,7 +374,7 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
   // 2. histogram of the low bits inside bin hi
   if (tid < kLoBins) sm.hist[tid] = 0u;
   __syncthreads();
-  for_each_key<FP16>(row, len, [&](int64_t, uint32_t o) {
+  ks.each([&](int64_t, uint32_t o) {
     if ((o >> kHiShift) == hi) atomicAdd(&sm.hist[o & (kLoBins - 1)], 1u);
   });
   __syncthreads();
@@ -219,24 +389,9 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
   const uint32_t t = sm.sel[2], g = sm.sel[3], need_eq = k - g;
 
   // 3. collect: keys above t anywhere in [0, g), the first need_eq keys equal to t in
-  // column order in [g, k)
-  const bool vec = ((uintptr_t)row & 15u) == 0u;
-  uint32_t eq_seen = 0u;   // keys equal to t in earlier runs (the same in every thread)
-  for (int64_t base = 0; base < len; base += (int64_t)kThreads * kRun) {
-    const int64_t i0 = base + (int64_t)tid * kRun;
-    uint32_t o[kRun];
-    if (vec && i0 + kRun <= len) {
-      const u32x4 v = *(const u32x4*)(row + i0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = order_key<FP16>(w[e] & 0xFFFFu);
-        o[2 * e + 1] = order_key<FP16>(w[e] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kRun; ++e) o[e] = i0 + e < len ? order_key<FP16>(row[i0 + e]) : 0u;   // real keys are never 0
-    }
+  // column order in [g, k) (steps cover consecutive column ranges, threads in column order)
+  uint32_t eq_seen = 0u;   // keys equal to t in earlier steps (the same in every thread)
+  gk.steps([&](int64_t i0, const uint32_t (&o)[kRun]) {
     uint32_t neq = 0u;
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
@@ -244,7 +399,7 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
       neq += o[e] == t ? 1u : 0u;
     }
     uint32_t total;
-    uint32_t r = eq_seen + block_exclusive_scan(neq, sm.wave_sums, &total);
+    uint32_t r = eq_seen + block_exclusive_scan<THREADS>(neq, sm.wave_sums, &total);
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
       if (o[e] == t) {
@@ -253,32 +408,41 @@ __device__ __forceinline__ uint32_t select_words(const uint16_t* row, int64_t co
       }
     }
     eq_seen += total;
-  }
+  });
   return k;
+}
+
+// Candidates of the span [col0, col0 + len) of a row (starting at `row`): from registers when
+// the span fits RUNS runs per thread, else from global memory on each pass.
+template <bool FP16, int THREADS, int RUNS>
+__device__ __forceinline__ uint32_t select_span(const uint16_t* row, int64_t col0, int64_t len, uint32_t kk,
+                                                TopkSmem& sm) {
+  const GlobalKeys<FP16, THREADS> gk{row, len};
+  if (len <= reg_cols<THREADS, RUNS>()) {
+    RegKeys<FP16, THREADS, RUNS> ks;
+    ks.load(row, len);
+    return select_words<FP16, THREADS>(ks, gk, col0, kk, sm);
+  }
+  return select_words<FP16, THREADS>(gk, gk, col0, kk, sm);
 }
 
 // One workgroup per row.
 template <bool FP16>
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TopkArgs a) {
+__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const TopkArgs a) {
   __shared__ TopkSmem sm;
   const int64_t r = blockIdx.x;
   const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride;
   const uint32_t k = (uint32_t)a.k;
-  const uint32_t m = select_words<FP16>(row, 0, a.n, k, sm);
-  emit_largest(sm.cand, m, k, [&](uint32_t j, unsigned long long w) { store_word<FP16>(w, j, k, r, a); });
+  const uint32_t m = select_span<FP16, kRowThreads, kRowRuns>(row, 0, a.n, k, sm);
+  emit_largest<kRowThreads>(sm.cand, m, k, [&](uint32_t j, unsigned long long w) { store_word<FP16>(w, j, k, r, a); });
 }
 
-// Rows cut into `parts` column chunks of `chunk` columns (a multiple of 8), one workgroup
-// per (chunk, row).  Each writes its chunk's k largest words (zero words past a short
-// chunk) to the workspace, then counts itself done on the row's counter; the row's last
-// workgroup sorts the parts * k words (at most kCand) and writes the row's result, then
-// clears the counter.  Ordering: every writer thread's words happen before the workgroup
-// barrier, which happens before thread 0's count; the count is an acquire-release
-// read-modify-write at device scope whose release half orders the workgroup's words before
-// it; the last workgroup's threads issue an acquire fence at device scope before reading the
-// words.
+// Rows cut into `parts` column chunks of `chunk` columns (a multiple of 8), one workgroup per
+// (chunk, row): each writes its chunk's k largest words to the workspace, largest first
+// (zero words after them when the chunk is shorter than k).
 template <bool FP16>
-__global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, const int parts, const int64_t chunk) {
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const TopkArgs a, const int parts,
+                                                                  const int64_t chunk) {
   __shared__ TopkSmem sm;
   const int c = blockIdx.x;
   const int64_t r = blockIdx.y;
@@ -287,39 +451,70 @@ __global__ __launch_bounds__(kThreads) void topk_parts_kernel(const TopkArgs a, 
   const int64_t len = a.n - col0 < chunk ? a.n - col0 : chunk;
   const uint32_t kk = (int64_t)k < len ? k : (uint32_t)len;
   const uint16_t* row = (const uint16_t*)a.logits + r * a.row_stride + col0;
-  const uint32_t mc = select_words<FP16>(row, col0, len, kk, sm);
-  unsigned int* counters = (unsigned int*)a.workspace;
-  unsigned long long* words = (unsigned long long*)a.workspace + kTopkWsHeader * a.rows + (r * parts + c) * (int64_t)k;
-  emit_largest(sm.cand, mc, kk, [&](uint32_t j, unsigned long long w) {
-    __hip_atomic_store(&words[j], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  });
-  for (uint32_t j = kk + threadIdx.x; j < k; j += kThreads)   // a chunk shorter than k
-    __hip_atomic_store(&words[j], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long* words = (unsigned long long*)a.workspace + r * kTopkWsRowWords + (int64_t)c * k;
+  const uint32_t m = select_span<FP16, kSelThreads, kSelRuns>(row, col0, len, kk, sm);
+  emit_largest<kSelThreads>(sm.cand, m, kk, [&](uint32_t j, unsigned long long w) { words[j] = w; });
+  for (uint32_t j = kk + threadIdx.x; j < k; j += kSelThreads) words[j] = 0ull;
+}
+
+// One workgroup per row: the row's parts lists of k words, each sorted largest first, are
+// merged.  A word's rank is its position in its own list plus, for every other list, the
+// number of larger words there (a binary search; the searches of kSearchLanes lists advance
+// together, so their LDS reads are in flight at once); the words of rank < k are the row's
+// result.  Zero words (padding of short chunks) are below every candidate and never ranked.
+constexpr int kSearchLanes = 8;
+template <bool FP16>
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const TopkArgs a, const int parts) {
+  __shared__ unsigned long long w[kMergeThreads];
+  const int64_t r = blockIdx.x;
+  const uint32_t k = (uint32_t)a.k;
+  const uint32_t m = (uint32_t)parts * k;   // at most kMergeThreads
+  const unsigned long long* src = (const unsigned long long*)a.workspace + r * kTopkWsRowWords;
+  const uint32_t i = threadIdx.x;
+  if (i < m) w[i] = src[i];
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned done = __hip_atomic_fetch_add(&counters[2 * r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = done + 1u == (unsigned)parts ? 1u : 0u;
+  if (i >= m) return;
+  const unsigned long long x = w[i];
+  if (x == 0ull) return;
+  const uint32_t p = i / k;
+  uint32_t rank = i - p * k;
+  int steps = 0;   // binary search steps over k entries
+  while ((1u << steps) <= k) ++steps;
+  for (uint32_t q0 = 0; q0 < (uint32_t)parts && rank < k; q0 += kSearchLanes) {
+    uint32_t lo[kSearchLanes], hi[kSearchLanes];
+#pragma unroll
+    for (int u = 0; u < kSearchLanes; ++u) {
+      const uint32_t q = q0 + u;
+      lo[u] = 0u;
+      hi[u] = (q < (uint32_t)parts && q != p) ? k : 0u;   // first entry not larger than x
+    }
+    for (int s = 0; s < steps; ++s) {
+#pragma unroll
+      for (int u = 0; u < kSearchLanes; ++u) {
+        if (lo[u] < hi[u]) {
+          const uint32_t mid = (lo[u] + hi[u]) >> 1;
+          if (w[(q0 + u) * k + mid] > x)
+            lo[u] = mid + 1u;
+          else
+            hi[u] = mid;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSearchLanes; ++u) rank += lo[u];
   }
-  __syncthreads();
-  if (sm.last == 0u) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const unsigned long long* row_words = (const unsigned long long*)a.workspace + kTopkWsHeader * a.rows + r * parts * (int64_t)k;
-  const uint32_t m = (uint32_t)parts * k;
-  for (uint32_t j = threadIdx.x; j < m; j += kThreads)
-    sm.cand[j] = __hip_atomic_load(&row_words[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  emit_largest(sm.cand, m, k, [&](uint32_t j, unsigned long long w) { store_word<FP16>(w, j, k, r, a); });
-  if (threadIdx.x == 0) __hip_atomic_store(&counters[2 * r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (rank < k) store_word<FP16>(x, rank, k, r, a);
 }
 
 }  // namespace
 
-// Columns per part: enough parts for about one workgroup per compute unit over all rows,
-// parts of at least 4096 columns, and parts * k within what one workgroup sorts.
+// Columns per chunk: about kTargetWorkgroups chunk workgroups over all rows, chunks of at
+// least kMinChunk columns, and parts * k within what the merge workgroup ranks.
 int64_t topk_chunk(int64_t n, int k, int64_t rows, int* parts) {
-  int64_t p = (256 + rows - 1) / rows;
-  const int64_t p_cols = (n + 4095) / 4096;
+  int64_t p = (kTargetWorkgroups + rows - 1) / rows;
+  const int64_t p_cols = (n + kMinChunk - 1) / kMinChunk;
   if (p > p_cols) p = p_cols;
-  const int64_t p_max = kCand / k;
+  const int64_t p_max = kMergeThreads / k;
   if (p > p_max) p = p_max;
   if (p < 1) p = 1;
   int64_t chunk = (n + p - 1) / p;
@@ -336,15 +531,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.workspace && parts > 1 && a.rows <= 65535) {
     const dim3 grid((unsigned)parts, (unsigned)a.rows);
     if (a.dtype == 2)
-      hipLaunchKernelGGL((topk_parts_kernel<true>), grid, dim3(kThreads), 0, stream, a, parts, chunk);
+      hipLaunchKernelGGL((topk_select_kernel<true>), grid, dim3(kSelThreads), 0, stream, a, parts, chunk);
     else
-      hipLaunchKernelGGL((topk_parts_kernel<false>), grid, dim3(kThreads), 0, stream, a, parts, chunk);
+      hipLaunchKernelGGL((topk_select_kernel<false>), grid, dim3(kSelThreads), 0, stream, a, parts, chunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.dtype == 2)
+      hipLaunchKernelGGL((topk_merge_kernel<true>), dim3((unsigned)a.rows), dim3(kMergeThreads), 0, stream, a, parts);
+    else
+      hipLaunchKernelGGL((topk_merge_kernel<false>), dim3((unsigned)a.rows), dim3(kMergeThreads), 0, stream, a, parts);
     return hipGetLastError();
   }
   if (a.dtype == 2)
-    hipLaunchKernelGGL((topk_rows_kernel<true>), dim3((unsigned)a.rows), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((topk_rows_kernel<true>), dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((topk_rows_kernel<false>), dim3((unsigned)a.rows), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((topk_rows_kernel<false>), dim3((unsigned)a.rows), dim3(kRowThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -9,9 +9,9 @@ namespace qmm {
 
 // Largest k the top-k kernel takes.
 constexpr int kTopkMax = 1024;
-// Workspace layout: per row a counter word pair (8 bytes), then per row 4096 candidate
-// words (8 bytes each): 8 + 32768 bytes per row.
-constexpr int64_t kTopkWsHeader = 1;        // 8-byte words of counters per row
+// Workspace layout: per row 4096 candidate words of 8 bytes (32768 bytes; the ABI's 32776
+// bytes per row leave 8 spare).  Every word the merge reads is written by the select kernel
+// of the same call, so the workspace needs no initial content.
 constexpr int64_t kTopkWsRowWords = 4096;   // candidate words per row
 
 struct TopkArgs {

@@ -220,14 +220,15 @@ int32_t qmm_qmv_argmax_noalloc(const void* x, const qmm_tensor_desc_t* x_desc, c
  * row_stride >= n.  out_index: DEVICE int32 [rows, k], 4-byte aligned; out_value: DEVICE
  * float32 [rows, k] or NULL.  Need 0 < n < 2^31, 0 <= rows < 2^31 and
  * 1 <= k <= min(n, QMM_TOPK_MAX) (QMM_ERR_SHAPE otherwise); rows == 0 is a no-op.
- * workspace: NULL, or DEVICE, 8-byte aligned, QMM_TOPK_WORKSPACE_BYTES(rows) bytes that are
- * ALL ZERO when the call's kernel starts (zero-fill once when allocated; the kernel leaves
- * the counters it uses zero again, so one workspace serves any number of calls in stream
- * order; calls that may overlap need workspaces of their own).  With a workspace, long rows
- * are split over several workgroups (column chunks of at least 4096, about one workgroup
- * per compute unit in all); without one, each row is one workgroup.  The results are the
- * same either way.
- * One kernel is enqueued; nothing is allocated. */
+ * workspace: NULL, or DEVICE, 8-byte aligned, QMM_TOPK_WORKSPACE_BYTES(rows) bytes of any
+ * content (the call writes every word it reads back; one workspace serves any number of
+ * calls in stream order; calls that may overlap need workspaces of their own).  With a
+ * workspace, long rows are split into column chunks of at least 2048 (about one chunk
+ * workgroup per compute unit in all, at most 1024 / k chunks per row): one kernel writes
+ * each chunk's k best candidates to the workspace and a second merges them per row.
+ * Without one, or when a row is not split, each row is one workgroup and one kernel.  The
+ * results are the same either way.
+ * One or two kernels are enqueued; nothing is allocated. */
 #define QMM_TOPK_MAX 1024
 #define QMM_TOPK_WORKSPACE_BYTES(rows) (32776 * (rows))
 int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int64_t row_stride, int32_t k,
@@ -236,7 +237,8 @@ int32_t qmm_topk(const void* logits, int32_t dtype, int64_t rows, int64_t n, int
 /* Decode with a per-row top-k: y = x . dequant(W)^T exactly as qmv (y is required and
  * dense, contract as for qmv), then qmm_topk over the rows of y (n = N, row_stride = N)
  * into out_index / out_value [rows, k], with `workspace` as for qmm_topk.  k is checked
- * before anything is enqueued.  Two kernels are enqueued. */
+ * before anything is enqueued.  The decode kernel and the top-k's one or two kernels are
+ * enqueued. */
 int32_t qmm_qmv_topk(const void* x, const qmm_tensor_desc_t* x_desc, const qmm_weight_desc_t* w, void* y,
                      const qmm_tensor_desc_t* y_desc, int32_t k, int32_t* out_index, float* out_value,
                      void* workspace, void* stream);
