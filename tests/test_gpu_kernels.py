@@ -58,6 +58,23 @@ def test_quantize_strided_rows(dev):
     assert np.array_equal(words(qw.w_packed), O.pack(ref["codes"], 4))
 
 
+@pytest.mark.parametrize("bits", [3, 5, 6, 8])
+def test_quantize_unaligned_stride_and_short_rows(dev, bits):
+    """Rows 4-byte but not 16-byte aligned (stride 517 floats: element-wise loads) and rows
+    that end inside a 256-element segment (K = 96 and 352, group 32), bit-exact."""
+    import bit_affine_quantized_qmv_amd as q
+    for k in (96, 352):
+        w = _rand_w(11, k, 40 + bits + k)
+        buf = torch.zeros(11, 517)
+        buf[:, :k] = torch.from_numpy(w)
+        qw = q.quantize(buf.to(dev)[:, :k], 32, bits, "fp16")
+        torch.cuda.synchronize()
+        ref = O.quantize(w, 32, bits, "fp16")
+        assert np.array_equal(words(qw.w_packed), O.pack(ref["codes"], bits)), k
+        assert np.array_equal(half_bits(qw.scales), ref["scales_bits"]), k
+        assert np.array_equal(half_bits(qw.biases), ref["biases_bits"]), k
+
+
 # ---------------------------------------------------------------- unpack probes
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("gs", GS)
