@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 import synth
-from qmm_testlib import (TORCH_DTYPE, assert_close, gather, half_bits, reference_rows,
+from qmm_testlib import (TORCH_DTYPE, assert_close, gather, half_bits, oracle_view_of, reference_rows,
                          require_gpu, upload_oracle_weight, values, words)
 
 pytestmark = pytest.mark.gpu
@@ -101,6 +101,18 @@ def test_odd_n_running_sum_workload(dev, case):
         assert np.all(yz == 0), (ODD_CASES[case], yz[:8])
 
 
+def _assert_all_outputs(y2d, x_rows, qw, dtype, slice_rows, what):
+    """Every output of a full-size call against the oracle, weight rows taken in slices."""
+    n = y2d.shape[1]
+    ov = oracle_view_of(qw)   # the weight copied to the host once
+    y_host = y2d.cpu()
+    for lo in range(0, n, slice_rows):
+        rows = np.arange(lo, min(n, lo + slice_rows))
+        ref = O.reference(x_rows, ov["w_packed"], ov["scales_bits"], ov["biases_bits"], qw.K, qw.group_size,
+                          qw.bits, dtype, rows=rows)
+        assert_close(y_host[:, lo:lo + len(rows)], ref, "%s, weight rows %d.." % (what, lo))
+
+
 def test_lm_head_full_size(dev):
     """lm_head decode at full size (x [32,1,1024], W [151936,1024], 4-bit, group 64, bf16):
     the GPU quantizer is bit-exact; the folded and the forced per-batch-element launches
@@ -120,6 +132,8 @@ def test_lm_head_full_size(dev):
     assert_close(y.reshape(cfg["m"], cfg["n"])[:, rows], ref, "lm_head")
     y1 = q.qmv(x[5], qw)
     assert torch.equal(y1[0], y[5, 0])
+    _assert_all_outputs(y.reshape(cfg["m"], cfg["n"]), values(x).reshape(cfg["m"], cfg["k"]), qw, cfg["dtype"],
+                        19000, "lm_head all outputs")
 
 
 def test_prefill_full_size(dev):
@@ -138,6 +152,8 @@ def test_prefill_full_size(dev):
     rows = synth.rows_sample(cfg["n"], 192, seed=2)
     ref = reference_rows(values(x).reshape(-1, cfg["k"]), qw, cfg["dtype"], rows=rows)
     assert_close(y.reshape(-1, cfg["n"])[:, rows], ref, "prefill contiguous")
+    _assert_all_outputs(y.reshape(-1, cfg["n"]), values(x).reshape(-1, cfg["k"]), qw, cfg["dtype"], 2048,
+                        "prefill all outputs")
     buf = synth.normal_x((cfg["b"], 2 * cfg["s"], cfg["k"]), cfg["dtype"], seed=cfg["buf_seed"]).to(dev)
     for start in (0, 256):
         view = buf[:, start:start + cfg["s"], :]
