@@ -1,6 +1,7 @@
 """GPU parity on the pages' workloads (synthetic values, the pages' shapes), including the
 full-size decode (lm_head) and prefill cases in the launch configuration the benchmark
-times.  Full-size outputs are checked on sampled weight rows against the oracle."""
+times.  Full-size outputs are checked against the oracle on sampled weight rows and then on
+every output, weight rows taken in slices."""
 import json
 import os
 
