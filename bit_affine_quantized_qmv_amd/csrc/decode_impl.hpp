@@ -447,16 +447,6 @@ __device__ inline int bias_span(int slots_per_row) {
   return (GS >= 64 && slots_per_row % 2 == 0) ? 2 : 1;
 }
 
-// Parts per row, a function of K, the weight's row count (N, times the experts of a gathered
-// stack), the code width and the group size only, so every decode kernel sums a row the same
-// way (part sums in k order, then added part by part) for every row count and plan of a call
-// on that weight.  Matrices of kFewRowsN rows or more:
-// the largest power of two <= min(8, slots/8), at least 1 (rows of at most 15 slots are not
-// cut).  Fewer rows (fewer tile pairs than two per compute unit): the largest power of two
-// <= min(8, slots / block_slots), so each wave walks as few slots as possible and the row's
-// latency shrinks (one 16-row tile of a K = 1024, 4-bit weight: 4 parts of 2 slots).
-constexpr int64_t kFewRowsN = 16384;
-
 // Rows of the weight a call reads from: N, or N per expert times the experts of a stack.
 __host__ __device__ inline int64_t weight_rows(const MatArgs& a) {
   return a.w_index ? a.N * a.num_experts : a.N;
@@ -465,13 +455,37 @@ __host__ __device__ inline int64_t weight_rows(const MatArgs& a) {
 // Sub-block size (slots) the decode kernels use for a row of nit slots.
 __host__ __device__ inline int block_slots(int nit) { return nit % 2 == 0 ? 2 : 1; }
 
+// Parts per row, a function of K, the weight's row count (N, times the experts of a gathered
+// stack), the code width and the group size only, so every decode kernel sums a row the same
+// way (part sums in k order, then added part by part) for every row count and plan of a call
+// on that weight.  P is the power of two <= 8 (parts of at least one sub-block) that
+// minimises a cost model of the launch: tile pairs are spread over at most 256 workgroups
+// of 8 waves, G = 8 / P pairs per workgroup and round, and a round costs a fixed overhead
+// (the parts' hand-off, 4 slot-equivalents) plus the slots one wave walks; ties go to more
+// parts.  P = 1 is the streaming kernel (whole rows per wave).  Few rows and long K get
+// many parts, many rows get whole rows per wave (the lm_head shape), e.g. one 16-row tile of
+// a K = 1024, 4-bit weight: 4 parts of 2 slots; N = 14336, K = 4096: 4 parts of 8 slots,
+// 224 workgroups of two pairs in one round (8 parts needed 1.75 rounds over 256).
 template <int BITS, int GS>
 __host__ __device__ inline int row_parts(int64_t K, int64_t N) {
-  const int64_t nit = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan;
-  const int step = N < kFewRowsN ? block_slots((int)nit) : 8;
-  int p = 1;
-  while (p < 8 && 2 * p * step <= nit) p *= 2;
-  return p;
+  const int nit = (int)((K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
+  const int d = block_slots(nit);
+  const int64_t n_pairs = ((N + 15) / 16 + 1) / 2;
+  int best_p = 1;
+  int64_t best_t = -1;
+  for (int p = 1; p <= 8; p *= 2) {
+    if (p > 1 && p * d > nit) break;
+    const int spp = p == 1 ? nit : (nit + p * d - 1) / (p * d) * d;
+    const int64_t g = 8 / p;
+    const int64_t wgs = (n_pairs + g - 1) / g < 256 ? (n_pairs + g - 1) / g : 256;
+    const int64_t rounds = (n_pairs + g * wgs - 1) / (g * wgs);
+    const int64_t t = rounds * (4 + spp);
+    if (best_t < 0 || t <= best_t) {
+      best_t = t;
+      best_p = p;
+    }
+  }
+  return best_p;
 }
 
 template <int BITS, int GS>

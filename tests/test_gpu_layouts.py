@@ -85,9 +85,9 @@ def test_pr_reproduction_shape(dev, rows):
         assert torch.equal(q.qmv(x[r], qw)[0], y[r, 0]), r
 
 
-# Shapes that reach each decode kernel path: whole rows at short K, rows cut into parts
-# (long K at 4 and 8 bits), activations too large for LDS (K processed in chunks), and
-# 17-32 rows at long K (two 16-row passes).
+# Shapes that reach each decode kernel path: whole rows per wave (wide weights), rows cut
+# into parts (narrower weights or long K), activations too large for LDS (K processed in
+# chunks), and 17-32 rows at long K (two 16-row passes).
 DET_CASES = [
     # (bits, gs, k, n, rows)
     (4, 64, 1024, 2000, 32),
@@ -100,6 +100,10 @@ DET_CASES = [
     (2, 32, 640, 1000, 16),
     (6, 32, 640, 1000, 1),
     (5, 64, 4096, 500, 32),
+    (4, 64, 1024, 65000, 32),    # whole rows per wave (streaming kernel)
+    (6, 32, 640, 65000, 16),
+    (2, 32, 640, 65000, 1),
+    (5, 64, 1024, 65000, 32),
 ]
 
 

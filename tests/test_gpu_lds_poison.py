@@ -98,9 +98,10 @@ def _quantized(q, dev, n, k, gs, bits, dtype, seed):
 
 DECODE_CASES = [
     # (bits, gs, k, n, rows, dtype): kernel path reached
-    (4, 64, 1024, 20000, 1, "bf16"),    # streaming, one row tile
-    (4, 64, 1024, 20000, 32, "bf16"),   # streaming, two row tiles
-    (3, 32, 640, 20000, 16, "fp16"),    # streaming, generic width
+    (4, 64, 1024, 65000, 1, "bf16"),    # streaming, one row tile
+    (4, 64, 1024, 65000, 32, "bf16"),   # streaming, two row tiles
+    (3, 32, 640, 65000, 16, "fp16"),    # streaming, generic width
+    (4, 64, 1024, 20000, 32, "bf16"),   # parts, 2 per row
     (4, 64, 1024, 3001, 32, "bf16"),    # parts (few weight rows)
     (4, 64, 2048, 1000, 8, "bf16"),     # parts
     (8, 64, 1024, 1000, 32, "fp16"),    # parts, 8-bit
