@@ -283,11 +283,14 @@ __device__ inline void generic_lane_offsets(int lg, int& word, uint32_t& shift) 
   shift = (uint32_t)(bit0 & 31);
 }
 
-// Staging of activation rows [0, MROWS) x k in [k_begin, k_begin + k_len) into LDS in MFMA
-// operand order: entry ((step * 4 + lane_group) * MROWS + m) holds 8 values.
+// Staging of activation rows [0, XR) x k in [k_begin, k_begin + k_len) into LDS in MFMA
+// operand order: entry ((step * 4 + lane_group) * XR + m) holds 8 values.  XR = 2^xrl LDS
+// rows (x_lds_rows_log2): all 16 * MT rows of the tiles, or the call's single row; operand
+// reads for tile row r use LDS row r mod XR, so rows of the tile past XR repeat earlier
+// rows, and their results are never stored.
 //
-// Thread t always handles activation row m = t % MROWS (the thread count is a multiple of
-// MROWS) and 8-k chunks j8 = t / MROWS, t / MROWS + nthreads / MROWS, ...  Loads are issued
+// Thread t always handles activation row m = t % XR (the thread count is a multiple of
+// XR) and 8-k chunks j8 = t / XR, t / XR + nthreads / XR, ...  Loads are issued
 // in batches of kStageBatch with clamped (always valid) addresses and no branches, so a
 // caller can issue a batch, then other loads, and only then wait for the batch: the memory
 // counter retires loads in issue order, and a load issued after the weight prefetch would
@@ -299,9 +302,18 @@ struct XStage {
   u32x4 v[kStageBatch];
 };
 
+// log2 of the activation rows staged in LDS for a call of `rows` rows (see above): two tiles
+// stage all 32 rows, one tile all 16 rows or, for a single activation row, that row alone
+// (so single-row calls fit in LDS up to K of about 64K).  A template parameter of the
+// kernels, so the operand addresses stay compile-time offsets.
+template <int MT>
+__host__ __device__ constexpr int x_lds_rows_log2(int rows) {
+  return MT != 1 ? 5 : (rows == 1 ? 0 : 4);
+}
+
 template <class T, int BITS, int MROWS>
-__device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb, int rows, int tid) {
-  const int m = tid % MROWS;
+__device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb, int rows, int tid, int xrl) {
+  const int m = tid & ((1 << xrl) - 1);
   const int mr = m < rows ? m : 0;   // rows past the call's rows read row 0, stored as zero
   // decode calls have at most 32 rows, so the segment arithmetic fits 32-bit integers
   const uint32_t sr = a.seg_rows < MROWS ? (uint32_t)a.seg_rows : (uint32_t)MROWS;
@@ -311,11 +323,11 @@ __device__ inline const uint16_t* stage_row(const MatArgs& a, const uint16_t* xb
 
 template <class T, int BITS, int MROWS>
 __device__ inline void stage_x_issue(XStage<MROWS>& st, const uint16_t* xr, int k_begin, int k_len, int batch,
-                                     int tid, int nthreads, int rows) {
+                                     int tid, int nthreads, int rows, int xrl) {
   const int c8 = k_len >> 3;
-  const int per = nthreads / MROWS;       // chunks advanced per pass
-  const int j0 = tid / MROWS + batch * kStageBatch * per;
-  const bool live = tid % MROWS < rows;   // padding rows are stored as zero without a load
+  const int per = nthreads >> xrl;        // chunks advanced per pass
+  const int j0 = (tid >> xrl) + batch * kStageBatch * per;
+  const bool live = (tid & ((1 << xrl) - 1)) < rows;   // padding rows are stored as zero without a load
 #pragma unroll
   for (int b = 0; b < kStageBatch; ++b) {
     int j8 = j0 + b * per;
@@ -326,18 +338,18 @@ __device__ inline void stage_x_issue(XStage<MROWS>& st, const uint16_t* xr, int 
 
 template <class T, int BITS, int MROWS>
 __device__ inline void stage_x_commit(const XStage<MROWS>& st, u32x4* xs, int rows, int k_len, int batch, int tid,
-                                      int nthreads) {
+                                      int nthreads, int xrl) {
   const int c8 = k_len >> 3;
-  const int per = nthreads / MROWS;
-  const int m = tid % MROWS;
-  const int j0 = tid / MROWS + batch * kStageBatch * per;
+  const int per = nthreads >> xrl;
+  const int m = tid & ((1 << xrl) - 1);
+  const int j0 = (tid >> xrl) + batch * kStageBatch * per;
 #pragma unroll
   for (int b = 0; b < kStageBatch; ++b) {
     const int j8 = j0 + b * per;
     if (j8 < c8) {
       u32x4 u = m < rows ? st.v[b] : u32x4{0u, 0u, 0u, 0u};
       if (BITS == 4) u = interleave_even_odd(u);
-      xs[((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) * MROWS + m] = u;
+      xs[(((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) << xrl) + m] = u;
     }
   }
 }
@@ -345,18 +357,17 @@ __device__ inline void stage_x_commit(const XStage<MROWS>& st, u32x4* xs, int ro
 // Zero the staged activations between k_len and k_pad (the last slot's k past K when K is
 // not a multiple of the slot span), so their products with whatever codes are loaded there
 // vanish.
-template <int BITS, int MROWS>
-__device__ inline void zero_x_pad(u32x4* xs, int k_len, int k_pad, int tid, int nthreads) {
-  const int per = nthreads / MROWS;
-  const int m = tid % MROWS;
-  for (int j8 = (k_len >> 3) + tid / MROWS; j8 < (k_pad >> 3); j8 += per)
-    xs[((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) * MROWS + m] = u32x4{0u, 0u, 0u, 0u};
+template <int BITS>
+__device__ inline void zero_x_pad(u32x4* xs, int k_len, int k_pad, int tid, int nthreads, int xrl) {
+  const int per = nthreads >> xrl;
+  const int m = tid & ((1 << xrl) - 1);
+  for (int j8 = (k_len >> 3) + (tid >> xrl); j8 < (k_pad >> 3); j8 += per)
+    xs[(((j8 >> 2) * 4 + lane_group_of_sub<BITS>(j8 & 3)) << xrl) + m] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // Number of staging batches for a chunk of k_len.
-template <int MROWS>
-__device__ inline int stage_batches(int k_len, int nthreads) {
-  const int per = nthreads / MROWS;
+__device__ inline int stage_batches(int k_len, int nthreads, int xrl) {
+  const int per = nthreads >> xrl;
   const int c8 = k_len >> 3;
   return (c8 + kStageBatch * per - 1) / (kStageBatch * per);
 }
@@ -364,32 +375,35 @@ __device__ inline int stage_batches(int k_len, int nthreads) {
 // Whole staging in one call (used where nothing is in flight that must not be waited for).
 template <class T, int BITS, int MROWS>
 __device__ inline void stage_x(u32x4* xs, const MatArgs& a, const uint16_t* xb, int rows, int k_begin,
-                               int k_len, int tid, int nthreads) {
-  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
-  const int nb = stage_batches<MROWS>(k_len, nthreads);
+                               int k_len, int tid, int nthreads, int xrl) {
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid, xrl);
+  const int nb = stage_batches(k_len, nthreads, xrl);
   for (int batch = 0; batch < nb; ++batch) {
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, k_begin, k_len, batch, tid, nthreads, rows);
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, k_len, batch, tid, nthreads);
+    stage_x_issue<T, BITS, MROWS>(st, xr, k_begin, k_len, batch, tid, nthreads, rows, xrl);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, k_len, batch, tid, nthreads, xrl);
   }
 }
 
 // Per (row, group) sums of the staged activations: MFMA against an all-ones operand, one
 // chain per (16-row tile, group), shared out over the workgroup's waves.  Layout
-// sxs[g * MROWS + m]; callers keep kSxPad zero groups after the last one, which the bias
-// MFMA of the final slot reads on its unused k lanes.
+// sxs[g * XR + m] for the XR staged rows; callers keep kSxPad zero groups after the last one,
+// which the bias MFMA of the final slot reads on its unused k lanes.
 constexpr int kSxPad = 3;
 
-template <int MT>
-__device__ inline void zero_sx_pad(float* sxs, int ng, int tid) {
-  constexpr int MROWS = 16 * MT;
-  if (tid < kSxPad * MROWS) sxs[ng * MROWS + tid] = 0.f;
+// Floats of the Σx area for ng groups and 2^xrl staged rows (with the padding groups), rounded
+// up to whole 16-byte units so that the 8-byte argmax keys (updated with 64-bit LDS atomics)
+// and the 16-byte hand-off entries placed after it are aligned.
+__host__ __device__ inline int sx_floats(int ng, int xrl) { return (((ng + kSxPad) << xrl) + 3) & ~3; }
+
+__device__ inline void zero_sx_pad(float* sxs, int ng, int tid, int xrl) {
+  if (tid < (kSxPad << xrl)) sxs[(ng << xrl) + tid] = 0.f;
 }
 
 template <class T, int GS, int MT>
-__device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, int nwaves, int lane) {
-  constexpr int MROWS = 16 * MT;
+__device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, int nwaves, int lane, int xrl) {
   constexpr int SPG = GS / 32;
+  const int xmask = (1 << xrl) - 1;
   const int lg = lane >> 4, col = lane & 15;
   const int ng = k_len / GS;
   const uint32_t one2 = T::pack2(1.0f, 1.0f);
@@ -400,8 +414,16 @@ __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, i
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < SPG; ++c)
-      d = T::mfma(as_v8<T>(xs[((g * SPG + c) * 4 + lg) * MROWS + mt * 16 + col]), as_v8<T>(ones), d);
-    if (col == 0) *(f32x4*)&sxs[g * MROWS + mt * 16 + 4 * lg] = d;
+      d = T::mfma(as_v8<T>(xs[(((g * SPG + c) * 4 + lg) << xrl) + ((mt * 16 + col) & xmask)]), as_v8<T>(ones), d);
+    if (col == 0) {
+      if (mt * 16 + 4 * lg + 3 <= xmask) {
+        *(f32x4*)&sxs[(g << xrl) + mt * 16 + 4 * lg] = d;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mt * 16 + 4 * lg + r <= xmask) sxs[(g << xrl) + mt * 16 + 4 * lg + r] = d[r];
+      }
+    }
   }
 }
 
@@ -417,11 +439,10 @@ __device__ inline void sum_x(const u32x4* xs, float* sxs, int k_len, int wave, i
 // covered; their A values are the next groups' sums or the zero padding, finite either way).
 template <class T, int MT, int TN>
 __device__ inline void bias_mfma(const uint32_t (&bh)[TN], const float* sxs, int g0, f32x4 (&acc)[TN][MT], int lg,
-                                 int col) {
-  constexpr int MROWS = 16 * MT;
+                                 int col, int xrl) {
   float sxa[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) sxa[mt] = sxs[(g0 + lg) * MROWS + mt * 16 + col];
+  for (int mt = 0; mt < MT; ++mt) sxa[mt] = sxs[((g0 + lg) << xrl) + ((mt * 16 + col) & ((1 << xrl) - 1))];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const float bv = T::to_f32(bh[t]);
@@ -500,9 +521,8 @@ template <class T, int BITS, int GS, int MT, int TN, int NH, bool BIAS = true>
 __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbRegs<NH> (&sc)[TN],
                                     const SbRegs<NH> (&bi)[TN], int hbase, const u32x4* xs, const float* sxs,
                                     int k_local, int k_valid, f32x4 (&acc)[TN][MT], f32x4 (&part)[TN][MT], int lg,
-                                    int col, uint32_t generic_shift) {
+                                    int col, uint32_t generic_shift, int xrl) {
   using S = Slot<BITS, GS>;
-  constexpr int MROWS = 16 * MT;
   constexpr int SPG = GS / 32;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   SlotCodes<BITS, GS> rc[TN];
@@ -516,7 +536,7 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
     for (int t = 0; t < TN; ++t) bq[t] = as_v8<T>(slot_codes<T, BITS, GS>(d[t], rc[t], c, generic_shift));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const typename T::v8 av = as_v8<T>(xs[((step0 + c) * 4 + lg) * MROWS + mt * 16 + col]);
+      const typename T::v8 av = as_v8<T>(xs[(((step0 + c) * 4 + lg) << xrl) + ((mt * 16 + col) & ((1 << xrl) - 1))]);
 #pragma unroll
       for (int t = 0; t < TN; ++t) part[t][mt] = T::mfma(av, bq[t], (c % SPG) == 0 ? zero4 : part[t][mt]);
     }
@@ -540,7 +560,7 @@ __device__ inline void consume_slot(const SlotData<BITS, GS> (&d)[TN], const SbR
     uint32_t bh[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) bh[t] = g_ok ? bi[t].template lane_half<S::kGroups>(hbase, lg) : 0u;
-    bias_mfma<T, MT, TN>(bh, sxs, k_local / GS, acc, lg, col);
+    bias_mfma<T, MT, TN>(bh, sxs, k_local / GS, acc, lg, col, xrl);
   }
 }
 

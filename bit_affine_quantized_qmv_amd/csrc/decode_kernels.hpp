@@ -29,7 +29,7 @@ constexpr int kPair = 2;         // weight tiles consumed together per slot
 constexpr int kRingFactor = 2;   // sub-blocks of weight loads in flight
 constexpr int kMaxWgPerCu = 8;   // cap on resident workgroups per compute unit in the grid size
 
-template <class T, int BITS, int GS, int MT, int D, bool SBB>
+template <class T, int BITS, int GS, int MT, int D, bool SBB, int XRL>
 __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_stream_kernel(const MatArgs a,
                                                                                      const int pairs_base,
                                                                                      const int pairs_rem) {
@@ -57,8 +57,9 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   extern __shared__ u32x4 smem[];
   const int K = (int)a.K;
   const int Kp = (K + S::kSpan - 1) / S::kSpan * S::kSpan;   // K rounded up to whole slots
+  constexpr int xrl = XRL;   // 2^xrl activation rows in LDS (x_lds_rows_log2)
   u32x4* xs = smem;
-  float* sxs = (float*)(smem + (Kp / 32) * 4 * MROWS);
+  float* sxs = (float*)(smem + (((Kp / 32) * 4) << xrl));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   const int nit = Kp / S::kSpan;             // slots per tile (a multiple of D)
   const int row_words = (K * BITS) >> 5;
   // fused argmax: per-row keys of the workgroup, after the activation sums
-  unsigned long long* kl = (unsigned long long*)(sxs + (K / GS + kSxPad) * MROWS);
+  unsigned long long* kl = (unsigned long long*)(sxs + sx_floats(K / GS, xrl));
   const bool do_argmax = a.argmax_keys != nullptr;
   const bool store_y = a.y != nullptr;
 
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   // loads, ahead of them in the queue, are not delayed by them.  (A wave still issuing
   // weight loads would hold up any barrier it has not reached, so none comes between the
   // prefetch and the staging waits.)  Larger activations are staged batch by batch first.
-  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
-  const int nbatch = stage_batches<MROWS>(K, kStreamThreads);
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid, xrl);
+  const int nbatch = stage_batches(K, kStreamThreads, xrl);
   auto prefetch = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SBB) issue_sb(scA, biA);
@@ -210,28 +211,28 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
     // activation loads first, the weight prefetch right behind them (loads return in issue
     // order, so waiting for the activations does not wait for the weights)
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows);
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows, xrl);
     // every wave's activation loads are issued before any weight load enters the queue
     lds_barrier();
     prefetch();
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
-    zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
-    zero_sx_pad<MT>(sxs, K / GS, tid);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads, xrl);
+    zero_x_pad<BITS>(xs, K, Kp, tid, kStreamThreads, xrl);
+    zero_sx_pad(sxs, K / GS, tid, xrl);
     if (do_argmax && tid < MROWS) kl[tid] = 0ull;
     lds_barrier();
-    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
+    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane, xrl);
     lds_barrier();
   } else {
     for (int batch = 0; batch < nbatch; ++batch) {
       XStage<MROWS> st;
-      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads, rows);
-      stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
+      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads, rows, xrl);
+      stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads, xrl);
     }
-    zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
-    zero_sx_pad<MT>(sxs, K / GS, tid);
+    zero_x_pad<BITS>(xs, K, Kp, tid, kStreamThreads, xrl);
+    zero_sx_pad(sxs, K / GS, tid, xrl);
     if (do_argmax && tid < MROWS) kl[tid] = 0ull;
     lds_barrier();
-    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
+    sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane, xrl);
     lds_barrier();
     prefetch();
   }
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
     for (int j = 0; j < D; ++j) {
       if constexpr (SBB) {
         consume_slot<T, BITS, GS, MT, TN, NHB, !kPairBias>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
-                                                           (c_kb + j) * S::kSpan, K, acc, part, lg, col, gshift);
+                                                           (c_kb + j) * S::kSpan, K, acc, part, lg, col, gshift, xrl);
         if (kPairBias && j % 2 == 1) {
           const int g0 = (c_kb + j - 1) * S::kSpan / GS;
           const bool g_ok = (g0 + lg) * GS < K;   // groups past K add nothing
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
 #pragma unroll
           for (int t = 0; t < TN; ++t)
             bh[t] = g_ok ? bi[t].template lane_half<2 * S::kGroups>((j - 1) * S::kGroups, lg) : 0u;
-          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
+          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col, xrl);
         }
       } else {
         SbRegs<S::kGroups> s1[TN], b1[TN];
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
         }
         consume_slot<T, BITS, GS, MT, TN, S::kGroups, !kPairBias>(ring[rbase + j], s1, b1, 0, xs, sxs,
                                                                   (c_kb + j) * S::kSpan, K, acc, part, lg, col,
-                                                                  gshift);
+                                                                  gshift, xrl);
         if (kPairBias && j % 2 == 0) {
 #pragma unroll
           for (int t = 0; t < TN; ++t) b_first[t] = b1[t];
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
           uint32_t bh[TN];
 #pragma unroll
           for (int t = 0; t < TN; ++t) bh[t] = g_ok ? pair_lane_half<S::kGroups>(b_first[t], b1[t], lg) : 0u;
-          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
+          bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col, xrl);
         }
       }
       if constexpr (!kDeepRing) {
@@ -370,6 +371,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
   __shared__ u32x4 xs[kChunkXBytes / 16];
   __shared__ float sxs[(KC / 32 + kSxPad) * MROWS];
   __shared__ unsigned long long kl[MROWS];
+  constexpr int xrl = MT == 1 ? 4 : 5;   // every row of the tiles staged
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -429,11 +431,11 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
     const int kcl = min(KC, K - kc0);
     lds_barrier();
     const int kclp = (kcl + S::kSpan - 1) / S::kSpan * S::kSpan;
-    stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads);
-    zero_x_pad<BITS, MROWS>(xs, kcl, kclp, tid, kThreads);
-    zero_sx_pad<MT>(sxs, kcl / GS, tid);
+    stage_x<T, BITS, MROWS>(xs, a, xb, rows, kc0, kcl, tid, kThreads, xrl);
+    zero_x_pad<BITS>(xs, kcl, kclp, tid, kThreads, xrl);
+    zero_sx_pad(sxs, kcl / GS, tid, xrl);
     lds_barrier();
-    sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane);
+    sum_x<T, GS, MT>(xs, sxs, kcl, wave, kWaves, lane, xrl);
     lds_barrier();
     const int kit0 = kc0 / S::kSpan;
     const int nit = kclp / S::kSpan;
@@ -449,10 +451,10 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
         }
         if (!pair_bias) {
           consume_slot<T, BITS, GS, MT, TN, S::kGroups>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, kcl, acc, part, lg,
-                                                        col, gshift);
+                                                        col, gshift, xrl);
         } else {
           consume_slot<T, BITS, GS, MT, TN, S::kGroups, false>(cur, sc, bi, 0, xs, sxs, i * S::kSpan, kcl, acc, part,
-                                                               lg, col, gshift);
+                                                               lg, col, gshift, xrl);
           if (kit % 2 == 0) {
 #pragma unroll
             for (int t = 0; t < TN; ++t) b_first[t] = bi[t];
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void qmv_chunk_kernel(const MatArgs a) {
             uint32_t bh[TN];
 #pragma unroll
             for (int t = 0; t < TN; ++t) bh[t] = g_ok ? pair_lane_half<S::kGroups>(b_first[t], bi[t], lg) : 0u;
-            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
+            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col, xrl);
           }
         }
       }
@@ -526,9 +528,9 @@ namespace decode {
 int device_cus();
 hipError_t kernel_wgs_per_cu(const void* kern, int threads, int lds, int lds_max, int* out);
 
-template <class T, int BITS, int GS, int MT, int D, bool SBB>
+template <class T, int BITS, int GS, int MT, int D, bool SBB, int XRL>
 hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
-  auto kern = qmv_stream_kernel<T, BITS, GS, MT, D, SBB>;
+  auto kern = qmv_stream_kernel<T, BITS, GS, MT, D, SBB, XRL>;
   int per_cu = 1;
   const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
   if (occ != hipSuccess) return occ;
@@ -544,29 +546,29 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
 }
 
 // Scales/biases per sub-block when their rows and bases are aligned to the load width.
-template <class T, int BITS, int GS, int MT, int D>
+template <class T, int BITS, int GS, int MT, int D, int XRL>
 hipError_t launch_stream_d(const MatArgs& a, hipStream_t stream, int lds) {
   if constexpr (BITS == 4 || BITS == 8) {
     constexpr int bytes = D * Slot<BITS, GS>::kGroups * 2;
     constexpr int align = bytes < 16 ? bytes : 16;
     if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
         (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
-      return launch_stream_sb<T, BITS, GS, MT, D, true>(a, stream, lds);
+      return launch_stream_sb<T, BITS, GS, MT, D, true, XRL>(a, stream, lds);
   }
-  return launch_stream_sb<T, BITS, GS, MT, D, false>(a, stream, lds);
+  return launch_stream_sb<T, BITS, GS, MT, D, false, XRL>(a, stream, lds);
 }
 
 // Slots per main-loop block (block_slots): 2 when the slots per tile are even, else 1.
-template <class T, int BITS, int GS, int MT>
+template <class T, int BITS, int GS, int MT, int XRL>
 hipError_t launch_stream(const MatArgs& a, hipStream_t stream, int lds) {
   const int nit = (int)((a.K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan);
-  if (block_slots(nit) == 2) return launch_stream_d<T, BITS, GS, MT, 2>(a, stream, lds);
-  return launch_stream_d<T, BITS, GS, MT, 1>(a, stream, lds);
+  if (block_slots(nit) == 2) return launch_stream_d<T, BITS, GS, MT, 2, XRL>(a, stream, lds);
+  return launch_stream_d<T, BITS, GS, MT, 1, XRL>(a, stream, lds);
 }
 
-template <class T, int BITS, int GS, int MT, int D, bool SBB>
+template <class T, int BITS, int GS, int MT, int D, bool SBB, int XRL>
 hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P, int spp) {
-  auto kern = qmv_parts_kernel<T, BITS, GS, MT, D, SBB>;
+  auto kern = qmv_parts_kernel<T, BITS, GS, MT, D, SBB, XRL>;
   int per_cu = 1;
   const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
   if (occ != hipSuccess) return occ;
@@ -579,7 +581,7 @@ hipError_t launch_parts_sb(const MatArgs& a, hipStream_t stream, int lds, int P,
   return hipGetLastError();
 }
 
-template <class T, int BITS, int GS, int MT>
+template <class T, int BITS, int GS, int MT, int XRL>
 hipError_t launch_parts(const MatArgs& a, hipStream_t stream, int lds) {
   const int P = row_parts<BITS, GS>(a.K, weight_rows(a));
   const int spp = part_slots<BITS, GS>(a.K, weight_rows(a));
@@ -590,18 +592,18 @@ hipError_t launch_parts(const MatArgs& a, hipStream_t stream, int lds) {
       constexpr int align = bytes < 16 ? bytes : 16;
       if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
           (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
-        return launch_parts_sb<T, BITS, GS, MT, 2, true>(a, stream, lds, P, spp);
+        return launch_parts_sb<T, BITS, GS, MT, 2, true, XRL>(a, stream, lds, P, spp);
     }
-    return launch_parts_sb<T, BITS, GS, MT, 2, false>(a, stream, lds, P, spp);
+    return launch_parts_sb<T, BITS, GS, MT, 2, false, XRL>(a, stream, lds, P, spp);
   }
   if constexpr (BITS == 4 || BITS == 8) {
     constexpr int bytes = Slot<BITS, GS>::kGroups * 2;
     constexpr int align = bytes < 16 ? bytes : 16;
     if ((a.sb_row_stride * 2) % align == 0 && (a.sb_expert_stride * 2) % align == 0 &&
         (uintptr_t)a.scales % align == 0 && (uintptr_t)a.biases % align == 0)
-      return launch_parts_sb<T, BITS, GS, MT, 1, true>(a, stream, lds, P, spp);
+      return launch_parts_sb<T, BITS, GS, MT, 1, true, XRL>(a, stream, lds, P, spp);
   }
-  return launch_parts_sb<T, BITS, GS, MT, 1, false>(a, stream, lds, P, spp);
+  return launch_parts_sb<T, BITS, GS, MT, 1, false, XRL>(a, stream, lds, P, spp);
 }
 
 template <class T, int BITS, int GS, int MT>
@@ -613,9 +615,9 @@ hipError_t launch_chunk(const MatArgs& a, hipStream_t stream) {
 }
 
 template <int BITS, int MT, int GS>
-constexpr int stream_lds_bytes(int K) {
+constexpr int stream_lds_bytes(int K, int xrl) {
   const int Kp = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan * Slot<BITS, GS>::kSpan;
-  return 16 * MT * Kp * 2 + (K / GS + kSxPad) * 16 * MT * 4 + 16 * MT * 8;
+  return ((Kp * 2) << xrl) + sx_floats(K / GS, xrl) * 4 + 16 * MT * 8;
 }
 
 template <class T, int BITS, int GS>
@@ -623,14 +625,23 @@ hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   const int K = (int)a.K;
   // long rows (see row_parts) run the parts kernel, the others the streaming kernel
   const bool parts = row_parts<BITS, GS>(K, weight_rows(a)) > 1;
-  const int lds1 = parts ? parts_lds_bytes<1, GS, BITS>(K) : stream_lds_bytes<BITS, 1, GS>(K);
-  const int lds2 = parts ? parts_lds_bytes<2, GS, BITS>(K) : stream_lds_bytes<BITS, 2, GS>(K);
+  // LDS of the one-tile kernels holds the power of two of activation rows covering the
+  // call's rows (x_lds_rows_log2), so short calls fit at long K
+  auto lds_one = [&](int64_t rows) {
+    const int xl = x_lds_rows_log2<1>((int)(rows < 16 ? rows : 16));
+    return parts ? parts_lds_bytes<1, GS, BITS>(K, xl) : stream_lds_bytes<BITS, 1, GS>(K, xl);
+  };
+  const int lds1 = lds_one(a.rows_per_batch);
+  const int lds2 = parts ? parts_lds_bytes<2, GS, BITS>(K, 5) : stream_lds_bytes<BITS, 2, GS>(K, 5);
   auto run1 = [&](const MatArgs& m) {
-    return parts ? launch_parts<T, BITS, GS, 1>(m, stream, lds1) : launch_stream<T, BITS, GS, 1>(m, stream, lds1);
+    const int lds = lds_one(m.rows_per_batch);
+    if (x_lds_rows_log2<1>((int)m.rows_per_batch) == 0)
+      return parts ? launch_parts<T, BITS, GS, 1, 0>(m, stream, lds) : launch_stream<T, BITS, GS, 1, 0>(m, stream, lds);
+    return parts ? launch_parts<T, BITS, GS, 1, 4>(m, stream, lds) : launch_stream<T, BITS, GS, 1, 4>(m, stream, lds);
   };
   if (a.rows_per_batch <= 16) return lds1 <= kLdsLimit ? run1(a) : launch_chunk<T, BITS, GS, 1>(a, stream);
   if (lds2 <= kLdsLimit)
-    return parts ? launch_parts<T, BITS, GS, 2>(a, stream, lds2) : launch_stream<T, BITS, GS, 2>(a, stream, lds2);
+    return parts ? launch_parts<T, BITS, GS, 2, 5>(a, stream, lds2) : launch_stream<T, BITS, GS, 2, 5>(a, stream, lds2);
   // 17..32 rows whose activations do not fit in LDS at once: when 16 activation rows do,
   // run the one-block kernel twice (rows 0..15, then the rest), which keeps every row's
   // arithmetic that of a call of at most 16 rows.  The second pass needs the rows to

@@ -6,7 +6,7 @@
 namespace qmm {
 namespace decode {
 
-template <class T, int BITS, int GS, int MT, int D, bool SBB>
+template <class T, int BITS, int GS, int MT, int D, bool SBB, int XRL>
 __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts_kernel(const MatArgs a, const int P,
                                                                                     const int spp) {
   // The workgroup's waves form G = 8/P groups of P waves.  Round r: group g works on tile
@@ -26,9 +26,10 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   extern __shared__ u32x4 smem[];
   const int K = (int)a.K;
   const int Kp = (K + S::kSpan - 1) / S::kSpan * S::kSpan;
+  constexpr int xrl = XRL;   // 2^xrl activation rows in LDS (x_lds_rows_log2)
   u32x4* xs = smem;
-  float* sxs = (float*)(smem + (Kp / 32) * 4 * MROWS);
-  unsigned long long* kl = (unsigned long long*)(sxs + (K / GS + kSxPad) * MROWS);
+  float* sxs = (float*)(smem + (((Kp / 32) * 4) << xrl));
+  unsigned long long* kl = (unsigned long long*)(sxs + sx_floats(K / GS, xrl));
   f32x4* hs = (f32x4*)(kl + MROWS);   // part sums handed to the group's wave 0
 
   const int tid = threadIdx.x;
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   };
 
   // ---- prologue: activation loads, barrier, weight prefetch, staging waits, sums
-  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid);
-  const int nbatch = stage_batches<MROWS>(K, kStreamThreads);
+  const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid, xrl);
+  const int nbatch = stage_batches(K, kStreamThreads, xrl);
   auto prefetch = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SBB) issue_sb(scA, biA);
@@ -172,22 +173,22 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   };
   if (nbatch == 1) {
     XStage<MROWS> st;
-    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows);
+    stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, 0, tid, kStreamThreads, rows, xrl);
     lds_barrier();
     prefetch();
-    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads);
+    stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, 0, tid, kStreamThreads, xrl);
   } else {
     for (int batch = 0; batch < nbatch; ++batch) {
       XStage<MROWS> st;
-      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads, rows);
-      stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads);
+      stage_x_issue<T, BITS, MROWS>(st, xr, 0, K, batch, tid, kStreamThreads, rows, xrl);
+      stage_x_commit<T, BITS, MROWS>(st, xs, rows, K, batch, tid, kStreamThreads, xrl);
     }
   }
-  zero_x_pad<BITS, MROWS>(xs, K, Kp, tid, kStreamThreads);
-  zero_sx_pad<MT>(sxs, K / GS, tid);
+  zero_x_pad<BITS>(xs, K, Kp, tid, kStreamThreads, xrl);
+  zero_sx_pad(sxs, K / GS, tid, xrl);
   if (do_argmax && tid < MROWS) kl[tid] = 0ull;
   lds_barrier();
-  sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane);
+  sum_x<T, GS, MT>(xs, sxs, K, wave, kStreamWaves, lane, xrl);
   lds_barrier();
   if (nbatch != 1) prefetch();
 
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
       if (real) {
         if constexpr (SBB) {
           consume_slot<T, BITS, GS, MT, TN, NHB, !kPairBias>(ring[rbase + j], sc, bi, j * S::kGroups, xs, sxs,
-                                                             (kit0 + j) * S::kSpan, K, acc, partial, lg, col, gshift);
+                                                             (kit0 + j) * S::kSpan, K, acc, partial, lg, col, gshift, xrl);
           if (kPairBias && j % 2 == 1) {
             const int g0 = (kit0 + j - 1) * S::kSpan / GS;
             const bool g_ok = (g0 + lg) * GS < K;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
 #pragma unroll
             for (int t = 0; t < TN; ++t)
               bh[t] = g_ok ? bi[t].template lane_half<2 * S::kGroups>((j - 1) * S::kGroups, lg) : 0u;
-            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
+            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col, xrl);
           }
         } else {
           SbRegs<S::kGroups> s1[TN], b1[TN];
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
           }
           consume_slot<T, BITS, GS, MT, TN, S::kGroups, !kPairBias>(ring[rbase + j], s1, b1, 0, xs, sxs,
                                                                     (kit0 + j) * S::kSpan, K, acc, partial, lg,
-                                                                    col, gshift);
+                                                                    col, gshift, xrl);
           if (kPairBias && j % 2 == 0) {
 #pragma unroll
             for (int t = 0; t < TN; ++t) b_first[t] = b1[t];
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
             uint32_t bh[TN];
 #pragma unroll
             for (int t = 0; t < TN; ++t) bh[t] = g_ok ? pair_lane_half<S::kGroups>(b_first[t], b1[t], lg) : 0u;
-            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col);
+            bias_mfma<T, MT, TN>(bh, sxs, g0, acc, lg, col, xrl);
           }
         }
       }
@@ -327,9 +328,9 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
 }
 
 template <int MT, int GS, int BITS>
-constexpr int parts_lds_bytes(int K) {
+constexpr int parts_lds_bytes(int K, int xrl) {
   const int Kp = (K + Slot<BITS, GS>::kSpan - 1) / Slot<BITS, GS>::kSpan * Slot<BITS, GS>::kSpan;
-  return 16 * MT * Kp * 2 + (K / GS + kSxPad) * 16 * MT * 4 + 16 * MT * 8 + kStreamWaves * kPair * MT * 64 * 16;
+  return ((Kp * 2) << xrl) + sx_floats(K / GS, xrl) * 4 + 16 * MT * 8 + kStreamWaves * kPair * MT * 64 * 16;
 }
 
 }  // namespace decode
