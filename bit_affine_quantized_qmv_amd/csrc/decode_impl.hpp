@@ -304,8 +304,9 @@ struct XStage {
 
 // log2 of the activation rows staged in LDS for a call of `rows` rows (see above): two tiles
 // stage all 32 rows, one tile all 16 rows or, for a single activation row, that row alone
-// (so single-row calls fit in LDS up to K of about 64K).  A template parameter of the
-// kernels, so the operand addresses stay compile-time offsets.
+// (so single-row calls fit in LDS up to K of about 64K); the launcher also stages 8 rows
+// for 2-8 rows whose 16-row staging does not fit.  A template parameter of the kernels, so
+// the operand addresses stay compile-time offsets.
 template <int MT>
 __host__ __device__ constexpr int x_lds_rows_log2(int rows) {
   return MT != 1 ? 5 : (rows == 1 ? 0 : 4);

@@ -1,12 +1,14 @@
 // Decode-family kernels and their launchers (instantiated per code width in decode_b*.hip).
 //
-// qmv_stream_kernel: the activations (all rows, all K) stay resident in LDS; every wave
-//   owns a contiguous range of 16-row weight tiles and streams them through a ring of
-//   DEPTH slots of in-flight 16-byte loads, so the HBM stream never waits on the MFMAs.
-//   The first loads are issued before the activations are staged.
+// qmv_stream_kernel: the staged activation rows (all K) stay resident in LDS; every wave
+//   owns a range of pairs of 16-row weight tiles and streams their whole rows through a
+//   register ring of in-flight 16-byte loads, so the HBM stream never waits on the MFMAs.
+//   The weight prefetch is issued right behind the activation loads.
+// qmv_parts_kernel (decode_parts.hpp): rows cut into parts along K, worked on by several
+//   waves at once (matrices with few rows or long K).
 // qmv_chunk_kernel: for activations too large for LDS; K is processed in chunks staged
 //   one after another, each wave keeping TN tiles' accumulators across chunks.
-// Both compute exactly the per-element arithmetic described in decode_impl.hpp.
+// All compute exactly the per-element arithmetic described in decode_impl.hpp.
 #pragma once
 
 #include <algorithm>
@@ -16,7 +18,7 @@
 namespace qmm {
 namespace decode {
 
-constexpr int kChunkTiles = 2;
+constexpr int kChunkTiles = 1;   // 16-row tiles per wave in the chunked kernel (more workgroups)
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kChunkXBytes = 64 * 1024;
 
@@ -625,18 +627,24 @@ hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   const int K = (int)a.K;
   // long rows (see row_parts) run the parts kernel, the others the streaming kernel
   const bool parts = row_parts<BITS, GS>(K, weight_rows(a)) > 1;
-  // LDS of the one-tile kernels holds the power of two of activation rows covering the
-  // call's rows (x_lds_rows_log2), so short calls fit at long K
-  auto lds_one = [&](int64_t rows) {
-    const int xl = x_lds_rows_log2<1>((int)(rows < 16 ? rows : 16));
+  // Activation rows the one-tile kernels stage in LDS (x_lds_rows_log2): one row alone, all
+  // 16 rows of the tile, or 8 rows for 2-8 rows whose 16-row staging does not fit
+  auto lds_at = [&](int xl) {
     return parts ? parts_lds_bytes<1, GS, BITS>(K, xl) : stream_lds_bytes<BITS, 1, GS>(K, xl);
   };
-  const int lds1 = lds_one(a.rows_per_batch);
+  auto xl_one = [&](int64_t rows) {
+    const int xl = x_lds_rows_log2<1>((int)(rows < 16 ? rows : 16));
+    return xl == 4 && rows <= 8 && lds_at(4) > kLdsLimit ? 3 : xl;
+  };
+  const int lds1 = lds_at(xl_one(a.rows_per_batch));
   const int lds2 = parts ? parts_lds_bytes<2, GS, BITS>(K, 5) : stream_lds_bytes<BITS, 2, GS>(K, 5);
   auto run1 = [&](const MatArgs& m) {
-    const int lds = lds_one(m.rows_per_batch);
-    if (x_lds_rows_log2<1>((int)m.rows_per_batch) == 0)
+    const int xl = xl_one(m.rows_per_batch);
+    const int lds = lds_at(xl);
+    if (xl == 0)
       return parts ? launch_parts<T, BITS, GS, 1, 0>(m, stream, lds) : launch_stream<T, BITS, GS, 1, 0>(m, stream, lds);
+    if (xl == 3)
+      return parts ? launch_parts<T, BITS, GS, 1, 3>(m, stream, lds) : launch_stream<T, BITS, GS, 1, 3>(m, stream, lds);
     return parts ? launch_parts<T, BITS, GS, 1, 4>(m, stream, lds) : launch_stream<T, BITS, GS, 1, 4>(m, stream, lds);
   };
   if (a.rows_per_batch <= 16) return lds1 <= kLdsLimit ? run1(a) : launch_chunk<T, BITS, GS, 1>(a, stream);

@@ -1,6 +1,6 @@
 """GPU parity of decode at long K with few activation rows.  A single-row call stages only
-that row in LDS, so it runs the streaming or parts kernels up to K of about 64K; 2-16 rows
-whose 16-row staging does not fit take the chunked kernel.  Each case is checked against
+that row in LDS, so it runs the streaming or parts kernels up to K of about 64K; 2-8 rows
+whose 16-row staging does not fit stage 8 rows, and the rest take the chunked kernel.  Each case is checked against
 the oracle, and every row of the call bit for bit against the same row called alone (the
 arithmetic of a row does not depend on how many rows share the call or which kernel runs
 it; mlx pull request 4516, "Correctness": bitwise identical results across batch sizes)."""
@@ -45,7 +45,7 @@ def test_long_k_few_rows(dev, case):
 
 
 @pytest.mark.parametrize("k,gs,rows", [(4096, 128, 1), (4096, 128, 2), (4096, 128, 3), (8192, 64, 1),
-                                       (4096, 128, 17)])
+                                       (4096, 128, 17), (8192, 64, 5)])
 def test_argmax_with_few_staged_rows(dev, k, gs, rows):
     """The fused argmax when one activation row is staged: its 8-byte LDS keys follow the
     per-group sums, whose float count (K / gs + 3 per staged row) can be odd, and must still
