@@ -34,7 +34,8 @@ constexpr int kMaxWgPerCu = 8;   // cap on resident workgroups per compute unit 
 template <class T, int BITS, int GS, int MT, int D, bool SBB, int XRL>
 __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_stream_kernel(const MatArgs a,
                                                                                      const int pairs_base,
-                                                                                     const int pairs_rem) {
+                                                                                     const int pairs_rem,
+                                                                                     const int y_area) {
   // The slots of a wave's tile pairs form one stream, consumed in sub-blocks of D slots (D
   // divides the slots per tile, so a pair always ends on a sub-block boundary).  Weight
   // loads run kRingFactor*D slots ahead of consumption (a ring of that many slots); with SBB the scales and
@@ -104,6 +105,10 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   unsigned long long* kl = (unsigned long long*)(sxs + sx_floats(K / GS, xrl));
   const bool do_argmax = a.argmax_keys != nullptr;
   const bool store_y = a.y != nullptr;
+  // whole tile pairs store through the wave's LDS area when the launch gave it one (it
+  // follows the argmax keys)
+  const bool y_vec = y_area != 0 && N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0u;
+  uint16_t* ys_area = (uint16_t*)(kl + MROWS) + wave * (MROWS * kYAreaStride);
 
   int gword = 0;
   uint32_t gshift = 0;
@@ -330,9 +335,13 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
         }
       }
       if (store_y) {
+        if (y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
+          store_pair_lds<T, MT>(acc, yb, rows, c_p * 16, N, ys_area, lane, lg, col);
+        } else {
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-          if (c_p + t < t_end) store_tile<T, MT>(acc[t], yb, rows, (c_p + t) * 16 + col, N, lg);
+          for (int t = 0; t < TN; ++t)
+            if (c_p + t < t_end) store_tile<T, MT>(acc[t], yb, rows, (c_p + t) * 16 + col, N, lg);
+        }
       }
 #pragma unroll
       for (int t = 0; t < TN; ++t)
@@ -536,6 +545,18 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
   int per_cu = 1;
   const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
   if (occ != hipSuccess) return occ;
+  // the output staging area, when the LDS has room for it at the same occupancy
+  int y_area = 0;
+  const int lds_y = lds + y_area_bytes<MT>(kStreamWaves);
+  if (a.y != nullptr && lds_y <= kLdsLimit) {
+    int per_cu_y = 0;
+    const hipError_t e = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds_y, kLdsLimit, &per_cu_y);
+    if (e != hipSuccess) return e;
+    if (std::min(per_cu_y, kMaxWgPerCu) == std::min(per_cu, kMaxWgPerCu)) {
+      y_area = 1;
+      lds = lds_y;
+    }
+  }
   // one full wave of workgroups (every CU at its occupancy), tile pairs spread over all waves
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
   const int64_t full = (int64_t)device_cus() * std::min(per_cu, kMaxWgPerCu);
@@ -543,7 +564,7 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
   const int64_t waves_total = blocks * kStreamWaves;
   if (n_pairs / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a,
-                     (int)(n_pairs / waves_total), (int)(n_pairs % waves_total));
+                     (int)(n_pairs / waves_total), (int)(n_pairs % waves_total), y_area);
   return hipGetLastError();
 }
 
