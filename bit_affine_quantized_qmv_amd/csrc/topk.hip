@@ -9,11 +9,16 @@
 // over the 16-bit values mapped to order keys (unsigned, larger key = larger value):
 //   0. spans of up to 8 * threads * 4 columns are loaded once into registers (8 consecutive
 //      columns per run, one 16-byte load when the row is 16-byte aligned, two keys per
-//      register); longer spans are read from global memory on each pass;
-//   1. with the keys in registers, a histogram of each thread's largest key over the key's
-//      high 11 bits gives a bin B that at least k of those maxima reach, so the k largest
-//      keys all lie in bin B or above; when those keys fit the candidate buffer (4096
-//      words, the usual case) they are the candidates;
+//      register, converted two at a time; runs past the span's end are skipped by whole
+//      waves); longer spans are read from global memory on each pass;
+//   1. with the keys in registers, a threshold t from the threads' largest keys: each wave
+//      finds the c = ceil(k / waves) largest of its threads' maxima (repeated wave maxima),
+//      and t is the k-th largest of all those values (a ballot radix select in one wave) or,
+//      when they do not fit one wave, the least of the waves' c-th values: at least k keys
+//      reach t either way.  The keys >= t are the candidates when there are at least k of
+//      them and they fit the candidate buffer (4096 words, the usual case); a wave collects
+//      them register by register, with one ballot test per register and one slot
+//      reservation per register that holds any;
 //   2. otherwise, a histogram of every key's high 11 bits (2048 bins, so that the values of
 //      a typical logit row spread over many LDS counters) -> the bin that holds the k-th
 //      largest key, found with a block-wide suffix count; at most 4096 keys in that bin and
@@ -26,8 +31,9 @@
 // many as threads by counting the larger words, beyond that by a bitonic sort in LDS; the
 // first k are the span's result.  With a workspace, long rows are cut into column chunks
 // (about one workgroup per compute unit in all): a select kernel writes each chunk's k
-// best words to the workspace, and a merge kernel, one workgroup per row, ranks the row's
-// parts * k words.  The kernel boundary orders the two, so no workgroup waits for another.
+// best words to the workspace, largest first, and a merge kernel, one workgroup per row,
+// merges the row's lists pairwise, level by level.  The kernel boundary orders the two, so
+// no workgroup waits for another.
 // The result does not depend on the order in which threads or workgroups run.
 #include <climits>
 
@@ -61,6 +67,56 @@ __device__ inline uint32_t order_key(uint32_t b) {
 }
 
 __device__ inline uint32_t key_bits(uint32_t o) { return (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu); }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Order keys of the two 16-bit values of w (low and high half) at once: the sign bit of each
+// half selects the mask (0xFFFF for negative values, 0x8000 for positive ones).  Exact for
+// every value but NaN, which the caller detects with has_nan2 and handles with order_key.
+__device__ inline uint32_t order_keys2(uint32_t w) {
+  const i16x2 s = __builtin_bit_cast(i16x2, w) >> (short)15;
+  return w ^ (__builtin_bit_cast(uint32_t, s) | 0x80008000u);
+}
+
+template <bool FP16>
+__device__ inline bool has_nan2(uint32_t w) {
+  constexpr uint32_t kInf2 = FP16 ? 0x7C007C00u : 0x7F807F80u;   // magnitudes above this are NaN
+  const u16x2 m = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w & 0x7FFF7FFFu), __builtin_bit_cast(u16x2, kInf2));
+  return __builtin_bit_cast(uint32_t, m) != kInf2;
+}
+
+// Largest v over the wave (in every lane): row-local DPP steps, then the row broadcasts.
+__device__ inline uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The k-th largest of the wave's nonzero 16-bit values u (one per lane), 0 when fewer than k
+// lanes hold one: a radix select from the top bit, counting lanes with ballots (the same
+// result in every lane).
+__device__ inline uint32_t wave_kth_largest(uint32_t u, uint32_t k) {
+  uint64_t cand = __builtin_amdgcn_ballot_w64(u != 0u);
+  if ((uint32_t)__builtin_popcountll(cand) < k) return 0u;
+  uint32_t prefix = 0u, need = k;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint64_t ones = __builtin_amdgcn_ballot_w64(((u >> bit) & 1u) != 0u) & cand;
+    const uint32_t n = (uint32_t)__builtin_popcountll(ones);
+    if (n >= need) {
+      cand = ones;
+      prefix |= 1u << bit;
+    } else {
+      need -= n;
+      cand &= ~ones;
+    }
+  }
+  return prefix;
+}
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets the sum.
 template <int THREADS>
@@ -144,22 +200,29 @@ struct GlobalKeys {
 
 // Keys of a span of at most reg_cols<THREADS, RUNS>() columns, loaded once into registers
 // with the same column assignment (run j of thread t: columns 8 * (t + THREADS * j) .. + 7),
-// two 16-bit keys per register (column 2e in the low half, 2e + 1 in the high half).
+// two 16-bit keys per register (column 2e in the low half, 2e + 1 in the high half).  Runs
+// that hold no column of any thread of the wave are skipped by the whole wave.
 template <bool FP16, int THREADS, int RUNS>
 struct RegKeys {
   static constexpr bool kHeldKeys = true;
   uint32_t p[RUNS][4];
+  int runs;   // runs holding a column of this wave's threads (the same in the whole wave)
   __device__ __forceinline__ static uint32_t pack(uint32_t w) {
     return order_key<FP16>(w & 0xFFFFu) | (order_key<FP16>(w >> 16) << 16);
   }
   __device__ __forceinline__ void load(const uint16_t* row, int64_t len) {
     const bool vec = ((uintptr_t)row & 15u) == 0u;
+    const int64_t wave_first = (int64_t)(__builtin_amdgcn_readfirstlane((int)threadIdx.x) & ~63);
+    runs = 0;
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j)
+      if ((int64_t)kRun * (wave_first + THREADS * j) < len) runs = j + 1;
     bool whole[RUNS];
     // every whole run's load is issued before any key is formed
 #pragma unroll
     for (int j = 0; j < RUNS; ++j) {
       const int64_t i0 = (int64_t)kRun * (threadIdx.x + THREADS * j);
-      whole[j] = vec && i0 + kRun <= len;
+      whole[j] = j < runs && vec && i0 + kRun <= len;
       if (whole[j]) {
         const u32x4 v = *(const u32x4*)(row + i0);
         p[j][0] = v.x;
@@ -168,12 +231,19 @@ struct RegKeys {
         p[j][3] = v.w;
       }
     }
+    bool nan = false;
 #pragma unroll
     for (int j = 0; j < RUNS; ++j) {
       const int64_t i0 = (int64_t)kRun * (threadIdx.x + THREADS * j);
-      if (whole[j]) {
+      if (j >= runs) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[j][e] = pack(p[j][e]);
+        for (int e = 0; e < 4; ++e) p[j][e] = 0u;
+      } else if (whole[j]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nan = nan || has_nan2<FP16>(p[j][e]);
+          p[j][e] = order_keys2(p[j][e]);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -184,25 +254,73 @@ struct RegKeys {
         }
       }
     }
+    if (nan) {   // a NaN among the thread's whole runs: their keys again, NaN by NaN
+#pragma unroll
+      for (int j = 0; j < RUNS; ++j) {
+        if (whole[j]) {
+          const u32x4 v = *(const u32x4*)(row + (int64_t)kRun * (threadIdx.x + THREADS * j));
+          p[j][0] = pack(v.x);
+          p[j][1] = pack(v.y);
+          p[j][2] = pack(v.z);
+          p[j][3] = pack(v.w);
+        }
+      }
+    }
   }
   // the thread's largest key (0 when it holds none)
   __device__ __forceinline__ uint32_t max_key() const {
-    uint32_t m = 0u;
+    u16x2 m = {0, 0};
 #pragma unroll
     for (int j = 0; j < RUNS; ++j)
+      if (j < runs)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m = max(m, max(p[j][e] & 0xFFFFu, p[j][e] >> 16));
-    return m;
+        for (int e = 0; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, p[j][e]));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+  }
+  // Writes the word of every key >= t (t > 0) to cand[*slot ...] (words past kCand are
+  // counted, not written), *slot counting them.  A register is looked at by the whole wave
+  // only when some lane's register holds such a key; then the wave reserves its slots with
+  // one atomic and places its lanes' keys by their rank in the ballots.
+  __device__ __forceinline__ void collect_ge(uint32_t t, int64_t col0, uint32_t* slot,
+                                             unsigned long long* cand) const {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t tt = (t - 1u) * 0x10001u;   // both halves t - 1: max(key, t - 1) > t - 1 iff key >= t
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j)
+      if (j < runs)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = p[j][e];
+          const u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w), __builtin_bit_cast(u16x2, tt));
+          if (__builtin_amdgcn_ballot_w64(__builtin_bit_cast(uint32_t, mx) != tt) != 0ull) {
+            const uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+            const uint64_t mlo = __builtin_amdgcn_ballot_w64(lo >= t);
+            const uint64_t mhi = __builtin_amdgcn_ballot_w64(hi >= t);
+            const uint32_t nlo = (uint32_t)__builtin_popcountll(mlo);
+            uint32_t base = 0u;
+            if (lane == 0u) base = atomicAdd(slot, nlo + (uint32_t)__builtin_popcountll(mhi));
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            const int64_t c = (int64_t)kRun * (threadIdx.x + THREADS * j) + 2 * e;
+            const uint32_t below = (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mlo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mlo, 0u));
+            const uint32_t below_hi = (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mhi >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mhi, 0u));
+            const uint32_t plo = base + below, phi = base + nlo + below_hi;
+            if (lo >= t && plo < (uint32_t)kCand)
+              cand[plo] = ((unsigned long long)lo << 32) | (0xFFFFFFFFu - (uint32_t)(col0 + c));
+            if (hi >= t && phi < (uint32_t)kCand)
+              cand[phi] = ((unsigned long long)hi << 32) | (0xFFFFFFFFu - (uint32_t)(col0 + c + 1));
+          }
+        }
   }
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
 #pragma unroll
     for (int j = 0; j < RUNS; ++j)
+      if (j < runs)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t o = (p[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        if (o) f((int64_t)kRun * (threadIdx.x + THREADS * j) + e, o);
-      }
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t o = (p[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          if (o) f((int64_t)kRun * (threadIdx.x + THREADS * j) + e, o);
+        }
   }
 };
 
@@ -210,6 +328,7 @@ struct RegKeys {
 struct TopkSmem {
   uint32_t hist[kHiBins];
   uint32_t wave_sums[16];
+  uint32_t top[64];
   uint32_t sel[4];
   uint32_t slot;
   unsigned long long cand[kCand];
@@ -324,32 +443,42 @@ __device__ __forceinline__ uint32_t select_words(const KS& ks, const GlobalKeys<
   };
 
   if constexpr (KS::kHeldKeys) {
-    // 0. A threshold from each thread's largest key: if the bin of the k-th largest of these
-    // maxima is B, at least k keys (those maxima, one per thread) lie in bin B or above, so
-    // the k largest keys do too.  One histogram update per thread instead of one per key;
-    // taken when the keys in bin B or above fit the candidate buffer (the usual case).
-    for (int b = tid; b < kHiBins; b += THREADS) sm.hist[b] = 0u;
+    // 0. A threshold from the threads' largest keys: each wave finds the c largest of its
+    // threads' maxima (c = ceil(k / waves)).  When the waves' c * waves values fit one wave,
+    // the threshold t is the k-th largest of them (maxima of distinct threads, so at least k
+    // keys reach it), else t = the least of the waves' c-th largest values (each wave has c
+    // keys reaching its own).  The keys >= t are the candidates when there are at least k of
+    // them and they fit the candidate buffer (the usual case; the count is checked, so the
+    // threshold needs no other guarantee), else the histogram passes below decide.  Each
+    // thread counts its candidates, reserves that many slots with one atomic, and writes
+    // them there.
+    constexpr uint32_t kWaves = THREADS / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t c = (k + kWaves - 1) / kWaves;
+    const bool pooled = kWaves * c <= 64u;
+    uint32_t v = (ks.max_key() << 6) | (uint32_t)lane;   // distinct per lane
+    uint32_t tw = 0u;
+    for (uint32_t i = 0; i < c; ++i) {
+      const uint32_t top = wave_max(v);
+      tw = top >> 6;
+      if (pooled && lane == 0) sm.top[wave * c + i] = tw;
+      if (v == top) v = 0u;   // that thread's maximum is taken
+    }
+    if (lane == 0) sm.wave_sums[wave] = tw;
+    if (tid == 0) sm.slot = 0u;
     __syncthreads();
-    const uint32_t mx = ks.max_key();
-    if (mx) atomicAdd(&sm.hist[mx >> kHiShift], 1u);
-    __syncthreads();
-    find_bin<THREADS>(k, sm);
-    if (sm.sel[2] >= k) {
-      // each thread counts its candidates, reserves that many slots with one atomic, and
-      // writes them there
-      const uint32_t lo_bin = sm.sel[0];
-      uint32_t cnt = 0u;
-      ks.each([&](int64_t, uint32_t o) { cnt += (o >> kHiShift) >= lo_bin ? 1u : 0u; });
-      uint32_t j = cnt ? atomicAdd(&sm.slot, cnt) : 0u;
-      ks.each([&](int64_t i, uint32_t o) {
-        if ((o >> kHiShift) >= lo_bin) {
-          if (j < (uint32_t)kCand) sm.cand[j] = word(o, i);
-          ++j;
-        }
-      });
+    uint32_t t = 0xFFFFFFFFu;
+    if (pooled) {
+      t = wave_kth_largest((uint32_t)lane < kWaves * c ? sm.top[lane] : 0u, k);
+    } else {
+#pragma unroll
+      for (uint32_t w = 0; w < kWaves; ++w) t = min(t, sm.wave_sums[w]);
+    }
+    if (t > 0u) {
+      ks.collect_ge(t, col0, &sm.slot, sm.cand);
       __syncthreads();
       const uint32_t m = sm.slot;
-      if (m <= (uint32_t)kCand) return m;
+      if (m >= k && m <= (uint32_t)kCand) return m;
       __syncthreads();   // every thread has read sm.slot before the histogram pass resets it
     }
   }
@@ -458,52 +587,56 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const TopkArgs
 }
 
 // One workgroup per row: the row's parts lists of k words, each sorted largest first, are
-// merged.  A word's rank is its position in its own list plus, for every other list, the
-// number of larger words there (a binary search; the searches of kSearchLanes lists advance
-// together, so their LDS reads are in flight at once); the words of rank < k are the row's
-// result.  Zero words (padding of short chunks) are below every candidate and never ranked.
-constexpr int kSearchLanes = 8;
+// merged pairwise, level by level, keeping the k largest of each pair (an odd list passes to
+// the next level as it is).  In a pair, a word's place is its index in its own list plus the
+// number of larger words in the other list (a binary search); the words are distinct (they
+// carry the column), so the places of the k largest are distinct.  Zero words (padding of
+// short chunks) are below every candidate: they only fill the places after the real words,
+// and the last level stores none of them.
 template <bool FP16>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const TopkArgs a, const int parts) {
-  __shared__ unsigned long long w[kMergeThreads];
+  __shared__ unsigned long long buf[2][kMergeThreads];
   const int64_t r = blockIdx.x;
   const uint32_t k = (uint32_t)a.k;
-  const uint32_t m = (uint32_t)parts * k;   // at most kMergeThreads
+  const uint32_t tid = threadIdx.x;
+  uint32_t nl = (uint32_t)parts;   // lists at this level, nl * k <= kMergeThreads
   const unsigned long long* src = (const unsigned long long*)a.workspace + r * kTopkWsRowWords;
-  const uint32_t i = threadIdx.x;
-  if (i < m) w[i] = src[i];
-  __syncthreads();
-  if (i >= m) return;
-  const unsigned long long x = w[i];
-  if (x == 0ull) return;
-  const uint32_t p = i / k;
-  uint32_t rank = i - p * k;
-  int steps = 0;   // binary search steps over k entries
-  while ((1u << steps) <= k) ++steps;
-  for (uint32_t q0 = 0; q0 < (uint32_t)parts && rank < k; q0 += kSearchLanes) {
-    uint32_t lo[kSearchLanes], hi[kSearchLanes];
-#pragma unroll
-    for (int u = 0; u < kSearchLanes; ++u) {
-      const uint32_t q = q0 + u;
-      lo[u] = 0u;
-      hi[u] = (q < (uint32_t)parts && q != p) ? k : 0u;   // first entry not larger than x
-    }
-    for (int s = 0; s < steps; ++s) {
-#pragma unroll
-      for (int u = 0; u < kSearchLanes; ++u) {
-        if (lo[u] < hi[u]) {
-          const uint32_t mid = (lo[u] + hi[u]) >> 1;
-          if (w[(q0 + u) * k + mid] > x)
-            lo[u] = mid + 1u;
+  if (tid < nl * k) buf[0][tid] = src[tid];
+  int cur = 0;
+  for (;;) {
+    __syncthreads();
+    const uint32_t pairs = nl >> 1, odd = nl & 1u;
+    const bool last = nl == 2u;
+    const unsigned long long* s = buf[cur];
+    unsigned long long* d = buf[cur ^ 1];
+    if (tid < nl * k) {
+      const uint32_t list = tid / k, i = tid - list * k;
+      const unsigned long long x = s[tid];
+      if (odd && list == nl - 1u) {
+        d[pairs * k + i] = x;
+      } else {
+        const unsigned long long* o = s + (list ^ 1u) * k;
+        uint32_t lo = 0u, hi = k;   // first entry of the other list not larger than x
+        while (lo < hi) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (o[mid] > x)
+            lo = mid + 1u;
           else
-            hi[u] = mid;
+            hi = mid;
+        }
+        const uint32_t pos = i + lo;
+        if (pos < k) {
+          if (!last)
+            d[(list >> 1) * k + pos] = x;
+          else if (x != 0ull)
+            store_word<FP16>(x, pos, k, r, a);
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kSearchLanes; ++u) rank += lo[u];
+    if (last) break;
+    nl = pairs + odd;
+    cur ^= 1;
   }
-  if (rank < k) store_word<FP16>(x, rank, k, r, a);
 }
 
 }  // namespace
