@@ -12,10 +12,10 @@
 //      register, converted two at a time; runs past the span's end are skipped by whole
 //      waves); longer spans are read from global memory on each pass;
 //   1. with the keys in registers, a threshold t from the threads' largest keys: each wave
-//      finds the c = ceil(k / waves) largest of its threads' maxima (repeated wave maxima),
-//      and t is the k-th largest of all those values (a ballot radix select in one wave) or,
-//      when they do not fit one wave, the least of the waves' c-th values: at least k keys
-//      reach t either way.  The keys >= t are the candidates when there are at least k of
+//      holding columns finds the c = ceil(k / such waves) largest of its threads' maxima
+//      (repeated wave maxima), and t is the k-th largest of all those values (a ballot
+//      radix select in one wave) or, when they do not fit one wave, the least of the waves'
+//      c-th values: at least k keys reach t either way.  The keys >= t are the candidates when there are at least k of
 //      them and they fit the candidate buffer (4096 words, the usual case); a wave collects
 //      them register by register, with one ballot test per register and one slot
 //      reservation per register that holds any;
@@ -443,8 +443,8 @@ __device__ __forceinline__ uint32_t select_words(const KS& ks, const GlobalKeys<
   };
 
   if constexpr (KS::kHeldKeys) {
-    // 0. A threshold from the threads' largest keys: each wave finds the c largest of its
-    // threads' maxima (c = ceil(k / waves)).  When the waves' c * waves values fit one wave,
+    // 0. A threshold from the threads' largest keys: each wave holding columns finds the c
+    // largest of its threads' maxima (c = ceil(k / such waves)).  When these values fit one wave,
     // the threshold t is the k-th largest of them (maxima of distinct threads, so at least k
     // keys reach it), else t = the least of the waves' c-th largest values (each wave has c
     // keys reaching its own).  The keys >= t are the candidates when there are at least k of
@@ -454,26 +454,36 @@ __device__ __forceinline__ uint32_t select_words(const KS& ks, const GlobalKeys<
     // them there.
     constexpr uint32_t kWaves = THREADS / 64;
     const int lane = tid & 63, wave = tid >> 6;
-    const uint32_t c = (k + kWaves - 1) / kWaves;
-    const bool pooled = kWaves * c <= 64u;
-    uint32_t v = (ks.max_key() << 6) | (uint32_t)lane;   // distinct per lane
-    uint32_t tw = 0u;
-    for (uint32_t i = 0; i < c; ++i) {
-      const uint32_t top = wave_max(v);
-      tw = top >> 6;
-      if (pooled && lane == 0) sm.top[wave * c + i] = tw;
-      if (v == top) v = 0u;   // that thread's maximum is taken
-    }
-    if (lane == 0) sm.wave_sums[wave] = tw;
-    if (tid == 0) sm.slot = 0u;
-    __syncthreads();
-    uint32_t t = 0xFFFFFFFFu;
-    if (pooled) {
-      t = wave_kth_largest((uint32_t)lane < kWaves * c ? sm.top[lane] : 0u, k);
-    } else {
-#pragma unroll
-      for (uint32_t w = 0; w < kWaves; ++w) t = min(t, sm.wave_sums[w]);
-    }
+    // computed over the first nw waves (those holding columns: the first run of wave w starts
+    // at column 64 * kRun * w); the copy for all waves has the count folded in
+    auto threshold = [&](const uint32_t nw) -> uint32_t {
+      const uint32_t c = (k + nw - 1) / nw;   // at most 64 threads per wave: c > 64 gives no threshold
+      const bool pooled = nw * c <= 64u;
+      uint32_t tw = 0u;
+      if ((uint32_t)wave < nw && c <= 64u) {
+        uint32_t v = (ks.max_key() << 6) | (uint32_t)lane;   // distinct per lane
+        for (uint32_t i = 0; i < c; ++i) {
+          const uint32_t top = wave_max(v);
+          tw = top >> 6;
+          if (pooled && lane == 0) sm.top[wave * c + i] = tw;
+          if (v == top) v = 0u;   // that thread's maximum is taken
+        }
+      }
+      if (lane == 0) sm.wave_sums[wave] = tw;
+      if (tid == 0) sm.slot = 0u;
+      __syncthreads();
+      if (c > 64u) return 0u;
+      if (pooled) return wave_kth_largest((uint32_t)lane < nw * c ? sm.top[lane] : 0u, k);
+      uint32_t least = 0xFFFFFFFFu;
+      for (uint32_t w = 0; w < nw; ++w) least = min(least, sm.wave_sums[w]);
+      return least;
+    };
+    // With waves that hold no columns, the copy for all waves still works when its pooled
+    // values from the waves that do hold columns number at least k (the others add zeros).
+    const uint32_t nw = gk.len >= (int64_t)THREADS * kRun ? kWaves : (uint32_t)((gk.len + 64 * kRun - 1) / (64 * kRun));
+    const uint32_t c_all = (k + kWaves - 1) / kWaves;
+    const bool all_works = nw == kWaves || (kWaves * c_all <= 64u && nw * c_all >= k);
+    const uint32_t t = all_works ? threshold(kWaves) : threshold(nw);
     if (t > 0u) {
       ks.collect_ge(t, col0, &sm.slot, sm.cand);
       __syncthreads();

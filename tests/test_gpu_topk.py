@@ -74,6 +74,34 @@ def test_topk_special_values(dtype):
         _check(logits, idx, val, k, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("k", [1, 64, 65])
+def test_topk_special_values_long_rows(dtype, k):
+    # rows cut into column chunks: NaN (of any payload and sign), infinities and signed zeros
+    # inside whole 8-column runs, where the keys are formed two at a time; k = 64 takes the
+    # threshold pooled over the waves' largest maxima, k = 65 the least of the waves' values
+    import bit_affine_quantized_qmv_amd as q
+    dev = require_gpu()
+    t = TORCH_DTYPE[dtype]
+    base = synth.normal_x((3, 20000), dtype, seed=1250).float()
+    base[0, [17, 4000, 15001]] = float("nan")
+    base[0, [8, 9, 19999]] = float("inf")
+    base[1, 100:9000:7] = float("-inf")
+    base[1, 5] = -0.0
+    base[2, :] = 0.0
+    base[2, 1::2] = -0.0
+    base[2, [3000, 12000]] = float("nan")
+    logits = base.to(t).to(dev)
+    raw = logits.view(torch.int16)
+    raw[0, 4000] = torch.tensor(-1, dtype=torch.int16)      # a negative NaN
+    raw[2, 12000] = torch.tensor(-2, dtype=torch.int16)     # another payload
+    ws = q.topk_workspace(3, dev)
+    for split in (True, False):
+        idx, val = q.topk(logits, k, workspace=ws if split else None, split=split)
+        torch.cuda.synchronize()
+        _check(logits, idx, val, k, dtype)
+
+
 def test_topk_strided_rows_and_k1_is_argmax_column():
     import bit_affine_quantized_qmv_amd as q
     dev = require_gpu()
