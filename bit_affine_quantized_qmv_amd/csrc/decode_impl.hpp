@@ -691,29 +691,40 @@ __device__ inline void store_tile(const f32x4 (&acc)[MT], uint16_t* yb, int rows
 }
 
 // The outputs of a whole tile pair (both tiles' rows below N, N a multiple of 8, y 16-byte
-// aligned) pass through the wave's LDS area of 16 * MT activation rows x kYAreaStride
-// halfwords: the MFMA layout (4 activation rows of one column per lane) becomes 8
-// consecutive columns of one activation row per lane, so the pair takes 16-byte stores
-// (2 * MT per lane instead of 8 * MT 2-byte ones).  The padded row stride spreads the four
-// lane groups' 2-byte writes over distinct banks.
+// aligned) pass through an LDS area of 16 * MT activation rows x kYAreaStride halfwords per
+// pair: the MFMA layout (4 activation rows of one column per lane) becomes 8 consecutive
+// columns of one activation row per lane, so the pair takes 16-byte stores (2 * MT per lane
+// instead of 8 * MT 2-byte ones).  The padded row stride spreads the four lane groups'
+// 2-byte writes over distinct banks.  A wave's area holds either one pair (stored right
+// away) or every pair of its range (stored after its weight stream ends, so no output
+// store waits in the wave's memory queue ahead of the weight refills).
 constexpr int kYAreaStride = 40;
 template <int MT>
-constexpr int y_area_bytes(int waves) { return waves * 16 * MT * kYAreaStride * 2; }
+constexpr int y_pair_halves() { return 16 * MT * kYAreaStride; }
+template <int MT>
+constexpr int y_area_bytes(int waves, int pairs) { return waves * pairs * y_pair_halves<MT>() * 2; }
 
 template <class T, int MT>
-__device__ inline void store_pair_lds(const f32x4 (&acc)[2][MT], uint16_t* yb, int rows, int64_t n0, int64_t N,
-                                      uint16_t* area, int lane, int lg, int col) {
+__device__ inline void stage_pair_lds(const f32x4 (&acc)[2][MT], uint16_t* area, int lg, int col) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) area[(mt * 16 + 4 * lg + r) * kYAreaStride + t * 16 + col] = T::from_f32(acc[t][mt][r]);
-  // the area is the wave's own: its LDS accesses complete in order, the fences only keep
-  // the compiler from moving them across one another
+}
+
+// the area is the wave's own: its LDS accesses complete in order, the fences only keep the
+// compiler from moving them across one another
+__device__ inline void wave_lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int MT>
+__device__ inline void flush_pair_lds(uint16_t* yb, int rows, int64_t n0, int64_t N, const uint16_t* area,
+                                      int lane) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + (lane >> 2);
@@ -721,9 +732,15 @@ __device__ inline void store_pair_lds(const f32x4 (&acc)[2][MT], uint16_t* yb, i
     const u32x4 v = *(const u32x4*)(area + m * kYAreaStride + c * 8);
     if (m < rows) *(u32x4*)(yb + (int64_t)m * N + n0 + c * 8) = v;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <class T, int MT>
+__device__ inline void store_pair_lds(const f32x4 (&acc)[2][MT], uint16_t* yb, int rows, int64_t n0, int64_t N,
+                                      uint16_t* area, int lane, int lg, int col) {
+  stage_pair_lds<T, MT>(acc, area, lg, col);
+  wave_lds_order();
+  flush_pair_lds<MT>(yb, rows, n0, N, area, lane);
+  wave_lds_order();
 }
 
 }  // namespace decode

@@ -105,10 +105,14 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   unsigned long long* kl = (unsigned long long*)(sxs + sx_floats(K / GS, xrl));
   const bool do_argmax = a.argmax_keys != nullptr;
   const bool store_y = a.y != nullptr;
-  // whole tile pairs store through the wave's LDS area when the launch gave it one (it
-  // follows the argmax keys)
+  // Whole tile pairs store through the wave's LDS area when the launch gave it one (it
+  // follows the argmax keys).  y_area is the number of pairs the area holds: 1 stores each
+  // pair as it completes; more (the launch then holds every pair of the wave's range) keeps
+  // them all and stores them after the wave's weight stream ends.
   const bool y_vec = y_area != 0 && N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0u;
-  uint16_t* ys_area = (uint16_t*)(kl + MROWS) + wave * (MROWS * kYAreaStride);
+  const bool y_defer = y_area > 1;
+  constexpr int kPairHalves = y_pair_halves<MT>();
+  uint16_t* ys_area = (uint16_t*)(kl + MROWS) + wave * (y_area * kPairHalves);
 
   int gword = 0;
   uint32_t gshift = 0;
@@ -336,7 +340,10 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
       }
       if (store_y) {
         if (y_vec && c_p + TN <= t_end && (c_p + TN) * 16 <= N) {
-          store_pair_lds<T, MT>(acc, yb, rows, c_p * 16, N, ys_area, lane, lg, col);
+          if (y_defer)
+            stage_pair_lds<T, MT>(acc, ys_area + (int)((c_p - t_begin) / TN) * kPairHalves, lg, col);
+          else
+            store_pair_lds<T, MT>(acc, yb, rows, c_p * 16, N, ys_area, lane, lg, col);
         } else {
 #pragma unroll
           for (int t = 0; t < TN; ++t)
@@ -365,6 +372,11 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
           sub_block((u % RF) * D, scB, biB, scA, biA);
       }
     }
+  }
+  if (store_y && y_vec && y_defer) {
+    wave_lds_order();
+    for (int64_t p = t_begin; p + TN <= t_end && (p + TN) * 16 <= N; p += TN)
+      flush_pair_lds<MT>(yb, rows, p * 16, N, ys_area + (int)((p - t_begin) / TN) * kPairHalves, lane);
   }
   if (do_argmax) {
     argmax_merge_wave<MT>(best, kl, lg, col);
@@ -545,24 +557,32 @@ hipError_t launch_stream_sb(const MatArgs& a, hipStream_t stream, int lds) {
   int per_cu = 1;
   const hipError_t occ = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds, kLdsLimit, &per_cu);
   if (occ != hipSuccess) return occ;
-  // the output staging area, when the LDS has room for it at the same occupancy
-  int y_area = 0;
-  const int lds_y = lds + y_area_bytes<MT>(kStreamWaves);
-  if (a.y != nullptr && lds_y <= kLdsLimit) {
-    int per_cu_y = 0;
-    const hipError_t e = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds_y, kLdsLimit, &per_cu_y);
-    if (e != hipSuccess) return e;
-    if (std::min(per_cu_y, kMaxWgPerCu) == std::min(per_cu, kMaxWgPerCu)) {
-      y_area = 1;
-      lds = lds_y;
-    }
-  }
   // one full wave of workgroups (every CU at its occupancy), tile pairs spread over all waves
   const int64_t n_pairs = ((a.N + 15) / 16 + kPair - 1) / kPair;
   const int64_t full = (int64_t)device_cus() * std::min(per_cu, kMaxWgPerCu);
   const int64_t blocks = std::min<int64_t>(full, (n_pairs + kStreamWaves - 1) / kStreamWaves);
   const int64_t waves_total = blocks * kStreamWaves;
   if (n_pairs / waves_total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // The output staging area, when the LDS has room for it at the same occupancy: every pair
+  // of a wave's range (stores after the weight stream), else one pair at a time.
+  int y_area = 0;
+  if (a.y != nullptr) {
+    const int64_t max_pairs = n_pairs / waves_total + (n_pairs % waves_total != 0 ? 1 : 0);
+    const int64_t tries[2] = {max_pairs > 1 ? max_pairs : 0, 1};
+    for (const int64_t yp : tries) {
+      if (yp < 1 || yp > 64) continue;
+      const int lds_y = lds + y_area_bytes<MT>(kStreamWaves, (int)yp);
+      if (lds_y > kLdsLimit) continue;
+      int per_cu_y = 0;
+      const hipError_t e = kernel_wgs_per_cu((const void*)kern, kStreamThreads, lds_y, kLdsLimit, &per_cu_y);
+      if (e != hipSuccess) return e;
+      if (std::min(per_cu_y, kMaxWgPerCu) == std::min(per_cu, kMaxWgPerCu)) {
+        y_area = (int)yp;
+        lds = lds_y;
+        break;
+      }
+    }
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, 1, (unsigned)a.batches), dim3(kStreamThreads), lds, stream, a,
                      (int)(n_pairs / waves_total), (int)(n_pairs % waves_total), y_area);
   return hipGetLastError();

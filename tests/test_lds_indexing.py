@@ -182,28 +182,36 @@ def check_shape(bits, gs, mt, xrl, K, parts=None):
         assert (hs_base4 + hs_entries) * 16 == parts_lds_bytes(bits, gs, mt, K, xrl)
 
 
-def check_y_area(mt, lds_bytes):
-    """store_pair_lds: wave w's area of 16 * mt rows x kYAreaStride halfwords after the keys;
-    the 2-byte writes and 16-byte reads stay inside it (and inside the launch's LDS)."""
+def check_y_area(mt, lds_bytes, pairs=1):
+    """stage_pair_lds / flush_pair_lds: wave w's area of `pairs` slots of 16 * mt rows x
+    kYAreaStride halfwords after the keys (one slot: each pair stored as it completes; more:
+    every pair of the wave's range kept until its stream ends); each slot's 16-byte reads
+    find all 8 halfwords written by that slot's 2-byte writes, and every access stays inside
+    the wave's own area and the launch's LDS."""
     rows_area = 16 * mt
+    pair_bytes = rows_area * Y_AREA_STRIDE * 2
     for wave in range(WAVES):
-        base = lds_bytes + wave * rows_area * Y_AREA_STRIDE * 2
-        written = set()
-        for lane in range(64):
-            lg, col = lane >> 4, lane & 15
-            for t in range(2):
-                for mtt in range(mt):
-                    for r in range(4):
-                        h = (mtt * 16 + 4 * lg + r) * Y_AREA_STRIDE + t * 16 + col
-                        written.add(base + 2 * h)
-        for mtt in range(mt):
+        lo = lds_bytes + wave * pairs * pair_bytes
+        hi = lo + pairs * pair_bytes
+        for q in range(pairs):
+            base = lo + q * pair_bytes
+            written = set()
             for lane in range(64):
-                m = mtt * 16 + (lane >> 2)
-                c = lane & 3
-                off = base + 2 * (m * Y_AREA_STRIDE + c * 8)
-                assert off % 16 == 0
-                assert all(off + 2 * i in written for i in range(8))   # all 8 halfwords written
-        assert max(written) + 2 <= lds_bytes + WAVES * rows_area * Y_AREA_STRIDE * 2
+                lg, col = lane >> 4, lane & 15
+                for t in range(2):
+                    for mtt in range(mt):
+                        for r in range(4):
+                            h = (mtt * 16 + 4 * lg + r) * Y_AREA_STRIDE + t * 16 + col
+                            written.add(base + 2 * h)
+            assert min(written) >= lo and max(written) + 2 <= hi
+            for mtt in range(mt):
+                for lane in range(64):
+                    m = mtt * 16 + (lane >> 2)
+                    c = lane & 3
+                    off = base + 2 * (m * Y_AREA_STRIDE + c * 8)
+                    assert off % 16 == 0
+                    assert all(off + 2 * i in written for i in range(8))   # all 8 halfwords written
+                    assert off + 16 <= hi
 
 
 # staged-row layouts the launchers use: (MT, XRL)
@@ -233,7 +241,8 @@ def test_parts_hand_off_reads_written_sums(bits, gs, parts):
 @pytest.mark.parametrize("mt,xrl", LAYOUTS)
 def test_output_staging_area_inside_lds(mt, xrl):
     for bits, gs, K in [(4, 64, 1024), (8, 32, 1408), (3, 32, 640)]:
-        check_y_area(mt, stream_lds_bytes(bits, gs, mt, K, xrl))
+        for pairs in (1, 2, 3):
+            check_y_area(mt, stream_lds_bytes(bits, gs, mt, K, xrl), pairs)
 
 
 def test_model_detects_a_missing_pad():
