@@ -105,6 +105,18 @@ UNALIGNED = {"n": 14336, "k": 4128, "b": 4, "s": 512, "bits": 4, "group_size": 3
              "dtype": "bf16", "w_seed": 900, "x_seed": 901, "w_std": 0.02}
 
 
+def random_packed_weight(n: int, row_words: int, groups: int, dtype: str, seed: int, scale_std: float = 1e-3,
+                         bias_std: float = 1e-3):
+    """A packed weight drawn directly, for shapes too large to quantize on the host: int32
+    [n, row_words] words with every bit pattern equally likely (so every code value occurs),
+    scales ~ N(0, scale_std^2) and biases ~ N(0, bias_std^2) [n, groups], stored in dtype."""
+    g = _gen(seed)
+    words = torch.randint(-2 ** 31, 2 ** 31, (n, row_words), generator=g, dtype=torch.int64).to(torch.int32)
+    scales = (torch.randn(n, groups, generator=g, dtype=torch.float32) * scale_std).to(TORCH_DTYPE[dtype])
+    biases = (torch.randn(n, groups, generator=g, dtype=torch.float32) * bias_std).to(TORCH_DTYPE[dtype])
+    return words, scales, biases
+
+
 def permutation(n: int, seed: int) -> torch.Tensor:
     """int32 seeded permutation of range(n)."""
     return torch.randperm(n, generator=_gen(seed)).to(torch.int32)

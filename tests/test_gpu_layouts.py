@@ -123,3 +123,24 @@ def test_repeated_calls_bitwise_equal_all_paths(dev, case, dtype):
         del junk
         y = q.qmv(x, qw)
         assert torch.equal(y, ref), (DET_CASES[case], dtype)
+
+
+@pytest.mark.parametrize("n", [262144, 327680])
+def test_decode_many_pairs_per_wave(dev, n):
+    """Weights long enough that each wave of the full decode grid (256 compute units) holds
+    four or five 32-row tile pairs (K = 1024, 4-bit, group 64, 32 activation rows): four
+    pairs' outputs fit the waves' LDS area and are stored after the weight stream, five do
+    not and are stored pair by pair.  Sampled weight rows (the last 64 included) within the
+    bound for all 32 rows, and rows 0, 17 and 31 bitwise equal to their one-row calls."""
+    import numpy as np
+    import bit_affine_quantized_qmv_amd as q
+    k, gs, bits, dtype = 1024, 64, 4, "bf16"
+    words, sc, bi = synth.random_packed_weight(n, k * bits // 32, k // gs, dtype, seed=1300 + n % 1000)
+    qw = q.QuantizedWeight(words.to(dev), sc.to(dev), bi.to(dev), n, k, gs, bits)
+    x = synth.normal_x((32, k), dtype, seed=1301).to(dev)
+    y = q.qmv(x, qw)
+    rows = np.unique(np.concatenate([synth.rows_sample(n, 768, seed=3), np.arange(n - 64, n)]))
+    ref = reference_rows(values(x), qw, dtype, rows=rows)
+    assert_close(y[:, rows], ref, "many pairs per wave, N=%d" % n)
+    for r in (0, 17, 31):
+        assert torch.equal(q.qmv(x[r:r + 1], qw)[0], y[r]), (n, r)
