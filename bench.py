@@ -268,7 +268,7 @@ def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
     res["unaligned_k"]["decode_32_rows"] = _leg(
         "unaligned-K qmv effective HBM GB/s", ubytes, tdd, "hbm", "GB/s", HBM_PEAK_GBS, "qmv_parts_kernel",
         {"workload": "decode qmv at unaligned K: x [32,1,4128] bf16 against the same W [14336,4128] 4-bit group 32 "
-                     "(last slot masked, rows cut into parts along K, two 16-row passes)",
+                     "(last slot masked, rows cut into parts along K, two 16-row blocks in one launch)",
          "algorithmic_bytes_per_call": ubytes})
     del uq, ux, uy, dx, dy
 

@@ -74,9 +74,9 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   const int col = lane & 15;
   const int64_t z = blockIdx.z;
   const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
-  const int rows = (int)a.rows_per_batch;
+  const int rows = (int)(a.last_rows != 0 && z == a.batches - 1 ? a.last_rows : a.rows_per_batch);
   const int64_t N = a.N;
-  uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
+  uint16_t* yb = (uint16_t*)a.y + z * a.rows_per_batch * N;
   const int w_row_bytes = (int)(a.w_row_stride * 4);
   const int sb_row_bytes = (int)(a.sb_row_stride * 2);
   const bool sb_narrow = sb_row_bytes % (2 * S::kGroups) != 0 || K % S::kSpan != 0;
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   if (do_argmax) {
     argmax_merge_wave<MT>(best, kl, lg, col);
     lds_barrier();
-    if (tid < rows) argmax_publish(&a.argmax_keys[z * rows + tid], kl[tid]);
+    if (tid < rows) argmax_publish(&a.argmax_keys[z * a.rows_per_batch + tid], kl[tid]);
     argmax_complete(a, a.batches * rows, (unsigned*)kl);   // kl is free again after the barrier inside
   }
 }
@@ -692,17 +692,28 @@ hipError_t launch_gs(const MatArgs& a, hipStream_t stream) {
   if (lds2 <= kLdsLimit)
     return parts ? launch_parts<T, BITS, GS, 2, 5>(a, stream, lds2) : launch_stream<T, BITS, GS, 2, 5>(a, stream, lds2);
   // 17..32 rows whose activations do not fit in LDS at once: when 16 activation rows do,
-  // run the one-block kernel twice (rows 0..15, then the rest), which keeps every row's
-  // arithmetic that of a call of at most 16 rows.  The second pass needs the rows to
+  // run the one-block kernel on rows 0..15 and on the rest, which keeps every row's
+  // arithmetic that of a call of at most 16 rows.  The second block needs the rows to
   // continue one 16-row block further at a fixed offset: one segment, or segments that are
-  // whole 16-row blocks; one grid slice.
+  // whole 16-row blocks; one grid slice.  Both blocks go in one launch, as two grid slices
+  // (the second with last_rows rows), so their workgroups run side by side; with a fused
+  // argmax (whose completion counts one launch's rows) they run one after the other.
   const int64_t rows = a.rows_per_batch;
   const bool one_seg = a.seg_rows >= rows;
   if (lds1 <= kLdsLimit && a.batches == 1 && (one_seg || a.seg_rows % 16 == 0)) {
+    const int64_t x_off = one_seg ? 16 * a.row_stride : (16 / a.seg_rows) * a.seg_stride + (16 % a.seg_rows) * a.row_stride;
+    if (a.argmax_keys == nullptr && a.w_index == nullptr) {
+      MatArgs two = a;
+      two.batches = 2;
+      two.batch_stride = x_off;
+      two.rows_per_batch = 16;
+      two.last_rows = rows - 16;
+      if (one_seg) two.seg_rows = 16;
+      return run1(two);
+    }
     MatArgs lo = a, hi = a;
     lo.rows_per_batch = 16;
     hi.rows_per_batch = rows - 16;
-    const int64_t x_off = one_seg ? 16 * a.row_stride : (16 / a.seg_rows) * a.seg_stride + (16 % a.seg_rows) * a.row_stride;
     hi.x = (const uint16_t*)a.x + x_off;
     if (one_seg) {
       lo.seg_rows = 16;

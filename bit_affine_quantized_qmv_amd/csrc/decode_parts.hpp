@@ -39,9 +39,9 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   const int col = lane & 15;
   const int64_t z = blockIdx.z;
   const uint16_t* xb = (const uint16_t*)a.x + z * a.batch_stride;
-  const int rows = (int)a.rows_per_batch;
+  const int rows = (int)(a.last_rows != 0 && z == a.batches - 1 ? a.last_rows : a.rows_per_batch);
   const int64_t N = a.N;
-  uint16_t* yb = (uint16_t*)a.y + z * (int64_t)rows * N;
+  uint16_t* yb = (uint16_t*)a.y + z * a.rows_per_batch * N;
   const int w_row_bytes = (int)(a.w_row_stride * 4);
   const int sb_row_bytes = (int)(a.sb_row_stride * 2);
   const bool sb_narrow = sb_row_bytes % (2 * S::kGroups) != 0 || K % S::kSpan != 0;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   if (do_argmax) {
     argmax_merge_wave<MT>(best, kl, lg, col);
     lds_barrier();
-    if (tid < rows) argmax_publish(&a.argmax_keys[z * rows + tid], kl[tid]);
+    if (tid < rows) argmax_publish(&a.argmax_keys[z * a.rows_per_batch + tid], kl[tid]);
     argmax_complete(a, a.batches * rows, (unsigned*)kl);
   }
 }

@@ -45,6 +45,10 @@ struct MatArgs {
   unsigned int* argmax_count = nullptr;
   int32_t* argmax_index = nullptr;
   float* argmax_value = nullptr;
+  // Rows of the last grid slice when it has fewer than rows_per_batch (0: every slice has
+  // rows_per_batch).  The decode family's 16-row blocks of a 17..32-row call use it; slice
+  // z's outputs still start at row z * rows_per_batch of y.
+  int64_t last_rows = 0;
 };
 
 struct QuantArgs {

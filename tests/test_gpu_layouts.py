@@ -87,7 +87,7 @@ def test_pr_reproduction_shape(dev, rows):
 
 # Shapes that reach each decode kernel path: whole rows per wave (wide weights), rows cut
 # into parts (narrower weights or long K), activations too large for LDS (K processed in
-# chunks), and 17-32 rows at long K (two 16-row passes).
+# chunks), and 17-32 rows at long K (two 16-row blocks).
 DET_CASES = [
     # (bits, gs, k, n, rows)
     (4, 64, 1024, 2000, 32),

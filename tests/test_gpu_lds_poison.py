@@ -10,7 +10,7 @@ test shows that the fill reaches the next dispatch at all (the hardware does not
 between dispatches), so that the others are not vacuous.
 
 Paths covered: the streaming decode kernel at one and two row tiles, the parts kernel, the
-chunked kernel, the two 16-row passes, every code width at the shapes with K = 640 and
+chunked kernel, the two 16-row blocks, every code width at the shapes with K = 640 and
 group 32 in fp16, the fused argmax, the gathered form, both prefill kernels, and top-k with
 and without column chunks."""
 import ctypes
@@ -106,7 +106,7 @@ DECODE_CASES = [
     (4, 64, 2048, 1000, 8, "bf16"),     # parts
     (8, 64, 1024, 1000, 32, "fp16"),    # parts, 8-bit
     (4, 128, 8192, 500, 16, "bf16"),    # chunked (activations beyond LDS)
-    (4, 32, 4096, 600, 32, "bf16"),     # two 16-row passes
+    (4, 32, 4096, 600, 32, "bf16"),     # two 16-row blocks
     (2, 32, 640, 1000, 16, "fp16"),
     (3, 32, 640, 1000, 16, "fp16"),
     (5, 32, 640, 1000, 1, "fp16"),
