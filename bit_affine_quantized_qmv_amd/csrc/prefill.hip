@@ -25,6 +25,58 @@ constexpr int BK = 64;            // k per main-loop step
 constexpr int WM = 4, WN = 2;     // waves along M and N; each wave owns a (BM/WM) x (BN/WN) tile
 constexpr int kThreads = 64 * WM * WN;
 
+// Epilogue: a wave's 64 x 128 outputs pass through 16 KB of LDS that the main loop no
+// longer reads, 32 rows at a time with a padded row stride (the four lane groups' 2-byte
+// writes land in distinct banks), and leave as 16-byte stores of 8 consecutive columns of
+// one output row; columns past N, or a y that does not allow 16-byte stores, take 2-byte
+// stores of the same values.
+constexpr int kYStride = 136;   // halfwords per staged output row (128 + 8)
+
+// the area is the wave's own: its LDS accesses complete in order, the fences only keep the
+// compiler from moving them across one another
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <class T, int FM, int FN>
+__device__ inline void store_wave_tile(const f32x4 (&acc)[FM][FN], uint16_t* area, uint16_t* yb, int64_t rows,
+                                       int64_t N, int64_t m0, int64_t n0, int lane, bool vec_ok) {
+  static_assert(FM == 4 && FN == 8, "a 64 x 128 wave tile, staged as two halves of 32 rows");
+  const int lg = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          area[(16 * ii + 4 * lg + r) * kYStride + 16 * j + col] = T::from_f32(acc[2 * h + ii][j][r]);
+    wave_lds_order();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = 4 * q + lg;
+      const u32x4 v = *(const u32x4*)(area + rr * kYStride + 8 * col);
+      const int64_t m = m0 + 32 * h + rr;
+      const int64_t n = n0 + 8 * col;
+      if (m < rows) {
+        uint16_t* dst = yb + m * N + n;
+        if (vec_ok && n + 8 <= N) {
+          *(u32x4*)dst = v;
+        } else {
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    wave_lds_order();
+  }
+}
+
 template <class T, int BITS>
 __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs a, const int m_tiles) {
   // operand layout in LDS: [buffer][k step (32)][lane group (8 k)][row] of 8 elements
@@ -162,17 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_kernel(const MatArgs 
     __syncthreads();
   }
 
+  // the main loop's last barrier is behind every LDS read of its operands: each wave takes
+  // 16 KB of the operand buffers for its outputs
   uint16_t* yb = (uint16_t*)a.y + z * rows * N;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = bm0 + wm * TM + 16 * i + 4 * lg + r;
-        const int64_t n = bn0 + wn * TN + 16 * j + col;
-        if (m < rows && n < N) yb[m * N + n] = T::from_f32(acc[i][j][r]);
-      }
+  const bool vec_ok = N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0u;
+  uint16_t* area = (uint16_t*)(wave < 4 ? (u32x4*)As : (u32x4*)Bs) + (wave & 3) * 8192;
+  store_wave_tile<T, FM, FN>(acc, area, yb, rows, N, bm0 + wm * TM, bn0 + wn * TN, lane, vec_ok);
 }
 
 // Bytes the activation descriptor of the direct-load kernel spans from a batch's first
@@ -373,17 +420,14 @@ __global__ __launch_bounds__(kThreads, 1) void qmm_prefill_dma_kernel(const MatA
     step(kt + 1, As1, As0, Bs1, Bs0, rwA, rsA, rbA);
   }
 
+  // the main loop's last barrier is behind every LDS read of its operands and every direct
+  // load into them: each wave takes 16 KB of the operand buffers for its outputs
   uint16_t* yb = (uint16_t*)a.y + z * rows * N;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = bm0 + wm * TM + 16 * i + 4 * lg + r;
-        const int64_t n = bn0 + wn * TN + 16 * j + col;
-        if (m < rows && n < N) yb[m * N + n] = T::from_f32(acc[i][j][r]);
-      }
+  const bool vec_ok = N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0u;
+  const int quarter = wave >> 1;
+  u32x4* const base = quarter == 0 ? As0 : quarter == 1 ? As1 : quarter == 2 ? &Bs0[0][0][0] : &Bs1[0][0][0];
+  uint16_t* area = (uint16_t*)base + (wave & 1) * 8192;
+  store_wave_tile<T, FM, FN>(acc, area, yb, rows, N, bm0 + wm * TM, bn0 + wn * TN, lane, vec_ok);
 }
 
 template <class T, int BITS>

@@ -258,3 +258,34 @@ def test_model_detects_a_missing_pad():
             check_shape(4, 128, 1, 4, 640)
     finally:
         SX_PAD = saved
+
+
+PREFILL_Y_STRIDE = 136   # kYStride in csrc/prefill.hip
+
+
+def test_prefill_epilogue_staging():
+    """store_wave_tile (csrc/prefill.hip): each wave stages its 64 x 128 outputs as two
+    halves of 32 rows in its own 16 KB of the operand buffers; every 16-byte read of a half
+    finds its 8 halfwords written by that half's 2-byte writes, reads are 16-byte aligned,
+    and every access stays inside the wave's 16 KB."""
+    region = 16 * 1024
+    for h in range(2):
+        written = {}
+        for lane in range(64):
+            lg, col = lane >> 4, lane & 15
+            for ii in range(2):
+                for j in range(8):
+                    for r in range(4):
+                        row_in_half = 16 * ii + 4 * lg + r
+                        off = 2 * (row_in_half * PREFILL_Y_STRIDE + 16 * j + col)
+                        assert off + 2 <= region
+                        assert off not in written
+                        written[off] = (32 * h + row_in_half, 16 * j + col)   # (tile row, tile column)
+        for q in range(8):
+            for lane in range(64):
+                lg, col = lane >> 4, lane & 15
+                rr = 4 * q + lg
+                off = 2 * (rr * PREFILL_Y_STRIDE + 8 * col)
+                assert off % 16 == 0 and off + 16 <= region
+                # the 8 halfwords are row 32h + rr, columns 8col .. 8col + 7, in order
+                assert [written[off + 2 * e] for e in range(8)] == [(32 * h + rr, 8 * col + e) for e in range(8)]
