@@ -71,6 +71,20 @@ struct Slot {
   static constexpr int kRowWordsPerSlot = kSpan * BITS / 32;
 };
 
+// Whether a slot's KG scale (or bias) halfwords of a row can be read as one load: every
+// row's, every expert's and both arrays' starts aligned to 2 * KG bytes.  Otherwise the
+// kernels read them one halfword at a time.
+template <int KG>
+__device__ inline bool sb_rows_aligned(const MatArgs& a) {
+  if constexpr (KG == 1) {
+    return true;
+  } else {
+    constexpr uint64_t w = 2 * KG;
+    return (((uintptr_t)a.scales | (uintptr_t)a.biases) % w) == 0 && (uint64_t)(a.sb_row_stride * 2) % w == 0 &&
+           (uint64_t)(a.sb_expert_stride * 2) % w == 0;
+  }
+}
+
 // Scale or bias values (raw 16-bit patterns) of NH consecutive groups of one weight row,
 // two per register.  get(h): halfword h (compile-time h).  lane_half<KG>(base, lg): the
 // value a lane feeds as k index lg of a bias MFMA covering the KG groups starting at

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   uint16_t* yb = (uint16_t*)a.y + z * a.rows_per_batch * N;
   const int w_row_bytes = (int)(a.w_row_stride * 4);
   const int sb_row_bytes = (int)(a.sb_row_stride * 2);
-  const bool sb_narrow = sb_row_bytes % (2 * S::kGroups) != 0 || K % S::kSpan != 0;
+  const bool sb_narrow = !sb_rows_aligned<S::kGroups>(a) || K % S::kSpan != 0;
   int w_voff[TN], sb_voff[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {

@@ -144,3 +144,28 @@ def test_decode_many_pairs_per_wave(dev, n):
     assert_close(y[:, rows], ref, "many pairs per wave, N=%d" % n)
     for r in (0, 17, 31):
         assert torch.equal(q.qmv(x[r:r + 1], qw)[0], y[r]), (n, r)
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 32), (4, 64), (8, 32), (8, 64)])
+@pytest.mark.parametrize("m", [1, 32])
+def test_decode_scales_two_bytes_off_alignment(dev, bits, gs, m):
+    """Scales and biases whose arrays start one halfword past a 4-byte boundary (views one
+    element into a buffer; rows of whole slots, so only the bases are off): the kernels read
+    them one halfword at a time, and the outputs are bitwise those of the same values at
+    aligned addresses and within the bound."""
+    import bit_affine_quantized_qmv_amd as q
+    n, k, dtype = 2000, 1024, "bf16"
+    g = k // gs
+    words, sc, bi = synth.random_packed_weight(n, k * bits // 32, g, dtype, seed=1400 + 10 * bits + gs)
+    qw = q.QuantizedWeight(words.to(dev), sc.to(dev), bi.to(dev), n, k, gs, bits)
+    sbuf = torch.zeros(n * g + 1, dtype=sc.dtype, device=dev)
+    bbuf = torch.zeros(n * g + 1, dtype=bi.dtype, device=dev)
+    sbuf[1:] = sc.reshape(-1).to(dev)
+    bbuf[1:] = bi.reshape(-1).to(dev)
+    qw_off = q.QuantizedWeight(qw.w_packed, sbuf[1:].view(n, g), bbuf[1:].view(n, g), n, k, gs, bits)
+    assert qw_off.scales.data_ptr() % 4 == 2 and qw_off.biases.data_ptr() % 4 == 2
+    x = synth.normal_x((m, k), dtype, seed=1401).to(dev)
+    y = q.qmv(x, qw)
+    y_off = q.qmv(x, qw_off)
+    assert torch.equal(y, y_off), (bits, gs, m)
+    assert_close(y_off, reference_rows(values(x), qw, dtype), "scales off alignment")
