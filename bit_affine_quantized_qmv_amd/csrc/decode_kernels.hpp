@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
       }
     }
   };
-  auto w_next = [&]() {
+  auto w_next = [&]() __attribute__((always_inline)) {
     w_kb += D;
     if (w_kb == nit) {
       w_kb = 0;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_strea
   // prefetch and the staging waits.)  Larger activations are staged batch by batch first.
   const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid, xrl);
   const int nbatch = stage_batches(K, kStreamThreads, xrl);
-  auto prefetch = [&]() {
+  auto prefetch = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SBB) issue_sb(scA, biA);
 #pragma unroll

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
       }
     }
   };
-  auto w_next = [&]() {
+  auto w_next = [&]() __attribute__((always_inline)) {
     if (++w_s == sbs) {
       w_s = 0;
       ++w_r;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamWavesPerSimd) void qmv_parts
   // ---- prologue: activation loads, barrier, weight prefetch, staging waits, sums
   const uint16_t* xr = stage_row<T, BITS, MROWS>(a, xb, rows, tid, xrl);
   const int nbatch = stage_batches(K, kStreamThreads, xrl);
-  auto prefetch = [&]() {
+  auto prefetch = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SBB) issue_sb(scA, biA);
 #pragma unroll

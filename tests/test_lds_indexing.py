@@ -30,7 +30,7 @@ def slot_span(bits, gs):
         return 128
     if bits == 8:
         return 128 if gs == 128 else 64
-    return gs
+    return 128
 
 
 def lane_group_of_sub(bits, sub):
