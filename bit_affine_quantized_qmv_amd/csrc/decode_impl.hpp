@@ -61,11 +61,12 @@ __device__ inline int lane_group_of_sub(int sub) {
 template <int BITS, int GS>
 struct Slot {
   // 4-bit: one 16-byte load per lane = 128 k of a row across the 4 lane groups.
-  // 8-bit: one 16-byte load per lane = 64 k; group 128 takes two.
-  // other widths: two words per lane per 32-k step, 128 k per slot at every group size (a
-  // slot then carries up to four groups, whose bias terms share one bias MFMA, and the
-  // per-slot loop overhead is paid once per 128 codes).
-  static constexpr int kSpan = BITS == 4 ? 128 : (BITS == 8 ? (GS == 128 ? 128 : 64) : 128);
+  // 8-bit: one 16-byte load per lane = 64 k; groups of 32 and 128 take two (128 k), groups
+  // of 64 one (the finer parts of 64-k slots measured faster for short rows there).
+  // other widths: two words per lane per 32-k step, 128 k per slot at every group size.
+  // A slot then carries up to four groups, whose bias terms share one bias MFMA, and the
+  // per-slot loop overhead is paid once per 128 codes.
+  static constexpr int kSpan = BITS == 8 && GS == 64 ? 64 : 128;
   static constexpr int kSteps = kSpan / 32;
   static constexpr int kGroups = kSpan / GS;                       // groups ending in a slot
   static constexpr int kVec = BITS == 4 ? 1 : (BITS == 8 ? kSpan / 64 : 0);   // u32x4 loads

@@ -26,11 +26,7 @@ Y_AREA_STRIDE = 40       # kYAreaStride (halfwords per activation row of the out
 
 def slot_span(bits, gs):
     """Slot<BITS, GS>::kSpan."""
-    if bits == 4:
-        return 128
-    if bits == 8:
-        return 128 if gs == 128 else 64
-    return 128
+    return 64 if bits == 8 and gs == 64 else 128
 
 
 def lane_group_of_sub(bits, sub):
