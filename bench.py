@@ -256,7 +256,7 @@ def _next_legs(args, q, torch, dev, synth, res, nsteps, nwarm):
     ux = synth.normal_x((uc["b"], uc["s"], uk), uc["dtype"], seed=uc["x_seed"]).to(dev)
     uy = torch.empty(uc["b"], uc["s"], un, dtype=ux.dtype, device=dev)
     flops = 2.0 * uc["b"] * uc["s"] * un * uk
-    tu = _time_steps(lambda i: q.qmm_t(ux, uq, out=uy), max(10, nsteps // 2), nwarm, torch, not args.no_graph)
+    tu = _time_steps(lambda i: q.qmm_t(ux, uq, out=uy), max(50, nsteps // 2), max(10, nwarm), torch, not args.no_graph)
     res["unaligned_k"] = _leg(
         "unaligned-K qmm_t TFLOP/s", flops, tu, "mfma", "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "qmm_prefill_dma_kernel",
         {"workload": "prefill qmm_t at unaligned K: x [4,512,4128] bf16, W [14336,4128] 4-bit group 32 "
@@ -553,9 +553,11 @@ def main():
         pxs = [px0.clone() for _ in range(pcopies)]
         pys = [torch.empty(bb, ss, pn, dtype=px0.dtype, device=dev) for _ in range(pcopies)]
         flops = 2.0 * bb * ss * pn * pk
-        psteps = max(10, args.steps // 4)
+        # at least 50 timed and 10 warm-up launches (about 12 ms of matrix-core work each way)
+        # whatever --steps says: shorter runs time the device's clock ramp, not the kernel
+        psteps = max(50, args.steps // 4)
         pt = _time_steps(lambda i: q.qmm_t(pxs[i % pcopies], pqs[i % pcopies], out=pys[i % pcopies]),
-                         psteps, max(3, args.warmup // 4), torch, not args.no_graph)
+                         psteps, max(10, args.warmup // 4), torch, not args.no_graph)
         buf = synth.normal_x((bb, 2 * ss, pk), pc["dtype"], seed=pc["buf_seed"]).to(dev)
         view = buf[:, 0:ss, :]
         pv = _time_steps(lambda i: q.qmm_t(view, pqs[i % pcopies], out=pys[i % pcopies]),
